@@ -1,0 +1,40 @@
+"""CPU oracle for weighted dynamic block-sparse attention — TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, fp64 NumPy statement of what the HIP path computes, written
+from the pages' description (InstaGen: group-shared importance sampling;
+AB-Attention: accurate block attention) and checked against closed forms,
+brute force and library routines by the CPU tests under ``tests/``.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it. The library and its Python binding never do: the
+product path has no CPU fallback. It shares no code with the HIP path; both
+sides are fed from the seeded generator in the package's ``inputs`` module,
+which holds none of the method's arithmetic.
+
+Modules, in the order the method runs:
+  scoring    block means and the estimated-attention score matrix S
+  selection  exact top-k set, inclusion probabilities, systematic sample, 1/pi weights
+  philox     the counter-based generator that supplies one offset per query block
+  attention  weighted sparse attention, dense attention, and the two HT sums
+
+Parity pins: every function here is pinned by at least one CPU test
+(``tests/test_oracle_*.py``); the one that is only self-consistent is noted in
+``philox`` (its canonical conformance is pinned by a cross-check against
+rocRAND's host-callable Philox4x32-10).
+"""
+
+from .philox import philox4x32_10, philox4x32_10_np, block_offset
+from .scoring import apply_perm, unpermute, valid_counts, block_means, score
+from .selection import (sanitize, exact_set, quantise, water_fill, fixed_point_pi,
+                        systematic_sample, inverse_weight, select_row, select, F_BITS, FS_BITS)
+from .attention import (attend, attend_block, attend_dense, dense_block, dense_row_max,
+                        unit_sums, weighted_sums)
+
+__all__ = [
+    "philox4x32_10", "philox4x32_10_np", "block_offset",
+    "apply_perm", "unpermute", "valid_counts", "block_means", "score",
+    "sanitize", "exact_set", "quantise", "water_fill", "fixed_point_pi",
+    "systematic_sample", "inverse_weight", "select_row", "select", "F_BITS", "FS_BITS",
+    "attend", "attend_block", "attend_dense", "dense_block", "dense_row_max",
+    "unit_sums", "weighted_sums",
+]
