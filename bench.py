@@ -1,0 +1,242 @@
+"""Benchmark: one weighted block-sparse attention layer per step on one MI355X.
+
+A step is the whole sparse pass -- bsa_score, bsa_select, bsa_attend -- over a
+synthetic clustered-token layer shaped like Wan2.1-T2V-14B at 720p (B=1, H=40,
+N=75,600 -> 75,648, d=128, bf16, 128-token blocks, 20 exact + 40 sampled key
+blocks per query block, ~10% density). Inputs are resident in HBM before the
+timed region. The dense flash-attention kernel of the same library is timed
+separately for the speedup.
+
+Prints one JSON line. `value` is milliseconds per layer (lower is better);
+`roofline` describes bsa_attend (bf16 MFMA bound), timed with HIP events on
+the stream it runs on; `cpu_baseline` is the fp64 CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ATTEND_SOURCE = os.path.join(ROOT, "block_sparse_attention_27_amd", "csrc", "attend_bf16.hip")
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attend_source_hash() -> str:
+    with open(ATTEND_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(workload: str):
+    """HBM bytes per bsa_attend launch from the committed counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"attend_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("attend_source_sha256_16") != attend_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, g, budget_s: float = 20.0):
+    """Time the oracle on a bounded sample and scale it to one layer (ms/layer)."""
+    import numpy as np
+    import oracle
+    from block_sparse_attention_27_amd.inputs import as_float32
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    h = 0
+    q = as_float32(g["q"][:, h:h + 1]).astype(np.float64)
+    k = as_float32(g["k"][:, h:h + 1]).astype(np.float64)
+    v = as_float32(g["v"][:, h:h + 1]).astype(np.float64)
+    t0 = time.perf_counter()
+    S, _, _ = oracle.score(q, k, w.N, w.block_q, w.block_k, w.sm_scale, g["perm"])
+    t_score_head = time.perf_counter() - t0
+    # selection: query blocks of head 0 in a spread order, for up to a quarter of the budget
+    order = list(range(0, w.n_qblocks, 7)) + [i for i in range(w.n_qblocks) if i % 7]
+    idx = np.zeros((1, 1, w.n_qblocks, w.list_len), np.int32)
+    wt = np.ones((1, 1, w.n_qblocks, w.list_len), np.float32)
+    t0 = time.perf_counter()
+    rows = []
+    for i in order:
+        (ri, rw), = oracle.select(S, w.N, w.block_k, w.k_exact, w.m_sample, w.select_seed, rows=[(0, 0, i)])
+        idx[0, 0, i], wt[0, 0, i] = ri, rw
+        rows.append(i)
+        if time.perf_counter() - t0 > budget_s / 4:
+            break
+    t_select_row = (time.perf_counter() - t0) / len(rows)
+    # attention: the same query blocks, for the rest of the budget
+    t0 = time.perf_counter()
+    done = 0
+    for i in rows:
+        oracle.attend(q, k, v, w.N, w.block_q, w.block_k, w.sm_scale, idx, wt, g["perm"], blocks=[(0, 0, i)])
+        done += 1
+        if time.perf_counter() - t0 > budget_s * 3 / 4:
+            break
+    t_attend_block = (time.perf_counter() - t0) / done
+    n_rows_total = w.B * w.H * w.n_qblocks
+    ms = 1e3 * (t_score_head * w.B * w.H + (t_select_row + t_attend_block) * n_rows_total)
+    sample = (f"head 0 of {w.H}: full score; select on {len(rows)} of {w.n_qblocks} query blocks; "
+              f"attend on {done} query blocks; scaled by (b,h) and query-block counts to the whole layer")
+    return {"value": round(ms, 1), "unit": "ms/layer", "cores": int(cores), "kind": "oracle",
+            "sample": sample,
+            "parts_s": {"score_per_head": round(t_score_head, 4), "select_per_block": round(t_select_row, 5),
+                        "attend_per_block": round(t_attend_block, 5)}}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="wan14b_720p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (--gpus {args.gpus} asked). "
+              "Heads shard across GPUs with no communication; run one process per GPU instead.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_27_amd as bsa
+    from block_sparse_attention_27_amd.inputs import WORKLOADS, generate
+
+    w = WORKLOADS[args.config]
+    _log(f"generating {w.name} inputs")
+    g = generate(w)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    q, k, v = dev(g["q"]), dev(g["k"]), dev(g["v"])
+    perm = torch.from_numpy(g["perm"]).cuda() if g["perm"] is not None else None
+    p = bsa.problem_for(w)
+    S = torch.empty((w.B, w.H, w.n_qblocks, w.n_units), dtype=torch.float32, device="cuda")
+    qm = torch.empty((w.B, w.H, w.n_qblocks, w.d), dtype=torch.float32, device="cuda")
+    km = torch.empty((w.B, w.H, w.n_units, w.d), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.B, w.H, w.n_qblocks, w.list_len), dtype=torch.int32, device="cuda")
+    wt = torch.empty((w.B, w.H, w.n_qblocks, w.list_len), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        bsa.bsa_score(p, q, k, perm, S, qm, km)
+        if ev: ev[1].record(stream)
+        bsa.bsa_select(p, S, idx, wt)
+        if ev: ev[2].record(stream)
+        bsa.bsa_attend(p, q, k, v, perm, idx, wt, out, None)
+        if ev: ev[3].record(stream)
+
+    _log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    _log(f"timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    t_score = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    t_select = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
+    t_attend = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
+    t_pass = statistics.mean(e[0].elapsed_time(e[3]) for e in evs)
+
+    t_dense = None
+    if not args.no_dense:
+        _log("timing the dense kernel")
+        outd = torch.empty_like(q)
+        for _ in range(2):
+            bsa.bsa_attend_dense(p, q, k, v, perm, outd, None)
+        n_dense = max(3, min(args.steps, 10))
+        de = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_dense)]
+        for e in de:
+            e[0].record(stream)
+            bsa.bsa_attend_dense(p, q, k, v, perm, outd, None)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        t_dense = statistics.mean(e[0].elapsed_time(e[1]) for e in de)
+        del outd
+
+    exec_flops = w.executed_flops()
+    dense_flops = w.dense_flops()
+    ach = exec_flops / (t_attend * 1e-3) / 1e12
+    elem = 2 if w.dtype == "bf16" else 4
+    score_bytes = 2 * w.B * w.H * w.N * w.d * elem + 4 * w.B * w.H * w.n_qblocks * w.n_units
+    select_bytes = 4 * w.B * w.H * w.n_qblocks * (w.n_valid_units + 2 * w.list_len)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, g)
+
+    rec = {
+        "metric": "sparse-attn ms/layer + executed MFMA TFLOP/s (% peak), Wan-14B shape, 10% density",
+        "value": round(t_pass, 4),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic clustered tokens (seeded), inputs resident in HBM",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_pad": w.N_pad, "d": w.d,
+                   "block_q": w.block_q, "block_k": w.block_k, "k_exact": w.k_exact,
+                   "m_sample": w.m_sample, "density": round(w.density, 4), "temperature": w.temperature,
+                   "permuted": w.permute, "parallelism": "single GPU"},
+        "t_score_ms": round(t_score, 4),
+        "t_select_ms": round(t_select, 4),
+        "t_attend_ms": round(t_attend, 4),
+        "t_dense_ms": None if t_dense is None else round(t_dense, 4),
+        "score_select_share": round((t_score + t_select) / t_pass, 4),
+        "executed_tflops": round(ach, 1),
+        "executed_frac_peak": round(ach / PEAK_BF16_TFLOPS, 4),
+        "dense_equiv_tflops": round(dense_flops / (t_pass * 1e-3) / 1e12, 1),
+        "dense_equiv_frac_peak": round(dense_flops / (t_pass * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "dense_kernel_tflops": None if t_dense is None else round(dense_flops / (t_dense * 1e-3) / 1e12, 1),
+        "speedup_vs_dense": None if t_dense is None else round(t_dense / t_pass, 3),
+        "score_hbm_gbs": round(score_bytes / (t_score * 1e-3) / 1e9, 1),
+        "select_hbm_gbs": round(select_bytes / (t_select * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "bsa_attend", "bound": "mfma", "achieved": round(ach, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic(w.name)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,249 @@
+"""Weighted dynamic block-sparse attention for video DiTs on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libbsa.so`` (declared in
+``include/bsa.h``). It only marshals torch tensors to device pointers and the
+current HIP stream; every step runs in the library's HIP kernels. There is no
+CPU fallback: if the library is missing, every call raises.
+
+Mirrors of the C entry points (same names and argument order, outputs passed
+in by the caller):
+    bsa_score(problem, q, k, perm, S, q_mean, k_mean)
+    bsa_select(problem, S, idx, w)
+    bsa_attend(problem, q, k, v, perm, idx, w, out, lse)
+    bsa_attend_dense(problem, q, k, v, perm, out, lse)
+Convenience wrappers that allocate their outputs: score, select, attend,
+attend_dense, sparse_attention (the three steps in order).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+from .inputs import Workload
+
+__all__ = [
+    "Problem", "BsaError", "load_library", "library_path", "problem_for",
+    "bsa_score", "bsa_select", "bsa_attend", "bsa_attend_dense",
+    "score", "select", "attend", "attend_dense", "sparse_attention",
+    "BSA_OK", "BSA_ERR_INVALID_ARG", "BSA_ERR_UNSUPPORTED", "BSA_ERR_HIP", "BSA_BF16", "BSA_FP32",
+]
+
+BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED, BSA_ERR_HIP = 0, 1, 2, 3
+BSA_BF16, BSA_FP32 = 0, 1
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.environ.get("BSA_LIBRARY", os.path.join(_PKG, "libbsa.so"))
+
+
+class Problem(ctypes.Structure):
+    """ctypes mirror of ``bsa_problem``."""
+
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("N_pad", ctypes.c_int32), ("d", ctypes.c_int32), ("block_q", ctypes.c_int32),
+        ("block_k", ctypes.c_int32), ("k_exact", ctypes.c_int32), ("m_sample", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("seed", ctypes.c_uint64), ("sm_scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+    @property
+    def nQB(self) -> int:
+        return self.N_pad // self.block_q
+
+    @property
+    def nKU(self) -> int:
+        return self.N_pad // self.block_k
+
+    @property
+    def L(self) -> int:
+        return self.k_exact + self.m_sample
+
+
+class BsaError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call} failed: {_status_text(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libbsa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libbsa.so not found at {path}: build it first "
+                           "(python -m block_sparse_attention_27_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, P = ctypes.c_void_p, ctypes.POINTER(Problem)
+    lib.bsa_abi_version.restype = ctypes.c_int32
+    lib.bsa_abi_version.argtypes = []
+    lib.bsa_status_string.restype = ctypes.c_char_p
+    lib.bsa_status_string.argtypes = [ctypes.c_int32]
+    lib.bsa_score.restype = ctypes.c_int
+    lib.bsa_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsa_select.restype = ctypes.c_int
+    lib.bsa_select.argtypes = [P, vp, vp, vp, vp]
+    lib.bsa_attend.restype = ctypes.c_int
+    lib.bsa_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsa_attend_dense.restype = ctypes.c_int
+    lib.bsa_attend_dense.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load_library().bsa_status_string(status).decode()
+    except Exception:  # the library itself may be what is missing
+        return "status"
+
+
+def problem_for(w: Workload, seed: Optional[int] = None, **overrides) -> Problem:
+    """A bsa_problem for a workload preset (overrides replace any field)."""
+    f = dict(B=w.B, H=w.H, N=w.N, N_pad=w.N_pad, d=w.d, block_q=w.block_q, block_k=w.block_k,
+             k_exact=w.k_exact, m_sample=w.m_sample,
+             dtype=BSA_BF16 if w.dtype == "bf16" else BSA_FP32,
+             seed=w.select_seed if seed is None else seed, sm_scale=w.sm_scale, reserved=0)
+    f.update(overrides)
+    return Problem(**f)
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _check(call: str, status: int):
+    if status != BSA_OK:
+        raise BsaError(call, status)
+
+
+def _elem_dtype(p: Problem):
+    import torch
+    return torch.bfloat16 if p.dtype == BSA_BF16 else torch.float32
+
+
+def _expect(name, t, shape, dtype):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name}: expected {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def bsa_score(p: Problem, q, k, perm, S, q_mean, k_mean, stream=None):
+    import torch
+    et = _elem_dtype(p)
+    qkv_shape = (p.B, p.H, p.N_pad, p.d)
+    _expect("q", q, qkv_shape, et); _expect("k", k, qkv_shape, et)
+    _expect("perm", perm, (p.N_pad,), torch.int32)
+    _expect("S", S, (p.B, p.H, p.nQB, p.nKU), torch.float32)
+    _expect("q_mean", q_mean, (p.B, p.H, p.nQB, p.d), torch.float32)
+    _expect("k_mean", k_mean, (p.B, p.H, p.nKU, p.d), torch.float32)
+    _check("bsa_score", load_library().bsa_score(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(perm), _ptr(S),
+                                                 _ptr(q_mean), _ptr(k_mean), _stream(stream)))
+
+
+def bsa_select(p: Problem, S, idx, w, stream=None):
+    import torch
+    _expect("S", S, (p.B, p.H, p.nQB, p.nKU), torch.float32)
+    _expect("idx", idx, (p.B, p.H, p.nQB, p.L), torch.int32)
+    _expect("w", w, (p.B, p.H, p.nQB, p.L), torch.float32)
+    _check("bsa_select", load_library().bsa_select(ctypes.byref(p), _ptr(S), _ptr(idx), _ptr(w),
+                                                   _stream(stream)))
+
+
+def bsa_attend(p: Problem, q, k, v, perm, idx, w, out, lse=None, stream=None):
+    import torch
+    et = _elem_dtype(p)
+    qkv_shape = (p.B, p.H, p.N_pad, p.d)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _expect(name, t, qkv_shape, et)
+    _expect("perm", perm, (p.N_pad,), torch.int32)
+    _expect("idx", idx, (p.B, p.H, p.nQB, p.L), torch.int32)
+    _expect("w", w, (p.B, p.H, p.nQB, p.L), torch.float32)
+    _expect("lse", lse, (p.B, p.H, p.N_pad), torch.float32)
+    _check("bsa_attend", load_library().bsa_attend(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(perm),
+                                                   _ptr(idx), _ptr(w), _ptr(out), _ptr(lse),
+                                                   _stream(stream)))
+
+
+def bsa_attend_dense(p: Problem, q, k, v, perm, out, lse=None, stream=None):
+    import torch
+    et = _elem_dtype(p)
+    qkv_shape = (p.B, p.H, p.N_pad, p.d)
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _expect(name, t, qkv_shape, et)
+    _expect("perm", perm, (p.N_pad,), torch.int32)
+    _expect("lse", lse, (p.B, p.H, p.N_pad), torch.float32)
+    _check("bsa_attend_dense", load_library().bsa_attend_dense(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                                               _ptr(perm), _ptr(out), _ptr(lse),
+                                                               _stream(stream)))
+
+
+# ---------------------------------------------------------------- convenience
+
+def score(p: Problem, q, k, perm=None, stream=None):
+    """Returns (S, q_mean, k_mean)."""
+    import torch
+    dev = q.device
+    S = torch.empty((p.B, p.H, p.nQB, p.nKU), dtype=torch.float32, device=dev)
+    qm = torch.empty((p.B, p.H, p.nQB, p.d), dtype=torch.float32, device=dev)
+    km = torch.empty((p.B, p.H, p.nKU, p.d), dtype=torch.float32, device=dev)
+    bsa_score(p, q, k, perm, S, qm, km, stream)
+    return S, qm, km
+
+
+def select(p: Problem, S, stream=None):
+    """Returns (idx, w)."""
+    import torch
+    idx = torch.empty((p.B, p.H, p.nQB, p.L), dtype=torch.int32, device=S.device)
+    w = torch.empty((p.B, p.H, p.nQB, p.L), dtype=torch.float32, device=S.device)
+    bsa_select(p, S, idx, w, stream)
+    return idx, w
+
+
+def attend(p: Problem, q, k, v, idx, w, perm=None, with_lse=False, stream=None):
+    """Returns out (and lse when ``with_lse``)."""
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty((p.B, p.H, p.N_pad), dtype=torch.float32, device=q.device) if with_lse else None
+    bsa_attend(p, q, k, v, perm, idx, w, out, lse, stream)
+    return (out, lse) if with_lse else out
+
+
+def attend_dense(p: Problem, q, k, v, perm=None, with_lse=False, stream=None):
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty((p.B, p.H, p.N_pad), dtype=torch.float32, device=q.device) if with_lse else None
+    bsa_attend_dense(p, q, k, v, perm, out, lse, stream)
+    return (out, lse) if with_lse else out
+
+
+def sparse_attention(p: Problem, q, k, v, perm=None, with_lse=False, stream=None):
+    """score -> select -> attend on one stream; returns (out[, lse], idx, w)."""
+    S, _, _ = score(p, q, k, perm, stream)
+    idx, w = select(p, S, stream)
+    res = attend(p, q, k, v, idx, w, perm, with_lse, stream)
+    return (res if isinstance(res, tuple) else (res,)) + (idx, w)

@@ -1,0 +1,46 @@
+// Internal declarations shared by the host API and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+// Geometry derived from a validated bsa_problem.
+struct Geometry {
+  int B, H, N, N_pad, d, block_q, block_k;
+  int nQB, nKU, n_valid_units, L;
+  bool bf16;
+  float sm_scale;
+  uint64_t seed;
+};
+
+// ---- scoring ----
+hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, const int32_t* perm,
+                              float* q_mean, float* k_mean, hipStream_t s);
+hipError_t launch_scores(const Geometry& g, const float* q_mean, const float* k_mean, float* S,
+                         hipStream_t s);
+
+// ---- selection ----
+hipError_t launch_select(const Geometry& g, int k_exact, int m_sample, const float* S, int32_t* idx,
+                         float* w, hipStream_t s);
+
+// ---- attention ----
+// idx/w == nullptr selects the dense variant (every valid key, weight 1).
+hipError_t launch_attend_bf16(const Geometry& g, const void* q, const void* k, const void* v,
+                              const int32_t* perm, const int32_t* idx, const float* w, void* out,
+                              float* lse, hipStream_t s);
+hipError_t launch_attend_fp32(const Geometry& g, const void* q, const void* k, const void* v,
+                              const int32_t* perm, const int32_t* idx, const float* w, void* out,
+                              float* lse, hipStream_t s);
+
+// Maps a hardware workgroup id onto a logical one so that each of the 8 XCDs
+// (which take workgroups round-robin) receives one contiguous logical range:
+// neighbouring query blocks of one head then share an XCD's L2.
+__device__ __forceinline__ int xcd_remap(int g, int total) {
+  const int per = total / 8, rem = total % 8;
+  const int x = g % 8;
+  return x * per + (x < rem ? x : rem) + g / 8;
+}
+
+}  // namespace bsa

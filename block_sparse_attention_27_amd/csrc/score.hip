@@ -1,0 +1,299 @@
+// Block scoring for gfx950: block means of Q and K, then the estimated
+// attention mass of every key unit for every query block.
+//
+// What is computed (AB-Attention, Abstract: blocks scored from coarse block
+// summaries; InstaGen, Abstract: a sample drawn in proportion to estimated
+// attention):
+//   q_mean_i = mean of the valid rows of query block i  (0 if it has none)
+//   k_mean_j = mean of the n_j valid keys of unit j
+//   S_ij     = n_j exp(l_ij - L_i) / sum_{valid j'} n_j' exp(l_ij' - L_i),
+//   l_ij = sm_scale <q_mean_i, k_mean_j>, L_i = max over valid j; S = 0 for
+//   units with no valid key.
+//
+// block_means_kernel streams Q and K once from HBM (16-byte loads, fp32
+// accumulation, one LDS reduction per block). scores_kernel contracts the
+// fp32 means with v_mfma_f32_32x32x2_f32 in the S^T orientation (a lane holds
+// one query block, its registers 16 units), so each lane keeps its own
+// running max and n_j-weighted sum; pass 1 stores the raw logits into S and
+// pass 2 rewrites them normalised.
+#include "bsa_internal.hpp"
+
+#include <math.h>
+
+namespace bsa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int MEAN_THREADS = 256;
+
+struct MeansArgs {
+  const void* q;
+  const void* k;
+  const int32_t* perm;
+  float* q_mean;
+  float* k_mean;
+  int N, N_pad, block_q, block_k, nQB, nKU, n_bh;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+// One workgroup per block of rows (a query block or a key unit).
+template <int D, bool BF16, bool PERM>
+__global__ __launch_bounds__(MEAN_THREADS) void block_means_kernel(MeansArgs a) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
+  constexpr int CH = D / EPC;                // chunks per row
+  constexpr int RPP = MEAN_THREADS / CH;     // rows per pass
+  __shared__ float red[RPP][D + 1];
+
+  const int tid = threadIdx.x;
+  const int nq = a.n_bh * a.nQB;
+  const bool is_q = static_cast<int>(blockIdx.x) < nq;
+  const int blk = is_q ? blockIdx.x : blockIdx.x - nq;
+  const int per = is_q ? a.nQB : a.nKU;
+  const int bs = is_q ? a.block_q : a.block_k;
+  const int bh = blk / per, bi = blk % per;
+  const char* base = static_cast<const char*>(is_q ? a.q : a.k) + static_cast<size_t>(bh) * a.N_pad * D * ESZ;
+  const int row0 = bi * bs;
+  const int nvalid = max(0, min(bs, a.N - row0));
+
+  constexpr int MAXP = 128 / RPP;  // passes for the largest block (128 rows)
+  const int cc = tid % CH, rg = tid / CH;
+  u32x4 x[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const int r = rg + p * RPP;
+    bool ok = r < nvalid;
+    int g = row0 + r;
+    if constexpr (PERM) {
+      if (ok) {
+        g = a.perm[g];
+        ok = static_cast<unsigned>(g) < static_cast<unsigned>(a.N_pad);
+      }
+    }
+    x[p] = ok ? *reinterpret_cast<const u32x4*>(base + (static_cast<size_t>(g) * D + cc * EPC) * ESZ)
+              : u32x4{0u, 0u, 0u, 0u};
+  }
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        acc[2 * z] += bf16_lo(x[p][z]);
+        acc[2 * z + 1] += bf16_hi(x[p][z]);
+      }
+    } else {
+#pragma unroll
+      for (int z = 0; z < 4; ++z) acc[z] += __uint_as_float(x[p][z]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) red[rg][cc * EPC + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) s += red[r][tid];
+    float* out = (is_q ? a.q_mean : a.k_mean) + (static_cast<size_t>(bh) * per + bi) * D;
+    out[tid] = nvalid > 0 ? s / static_cast<float>(nvalid) : 0.f;
+  }
+}
+
+struct ScoreArgs {
+  const float* q_mean;
+  const float* k_mean;
+  float* S;
+  int N, block_k, nQB, nKU, n_qgroups;
+  float sm_scale;
+};
+
+constexpr int SC_WAVES = 4;
+
+// One workgroup per (b, h, group of 32 query blocks); wave w takes unit chunks
+// w, w + 4, ... (32 units each).
+template <int D>
+__global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
+  constexpr int HALF = D / 2;  // lane half h contracts d in [h*HALF, (h+1)*HALF)
+  __shared__ float red_m[SC_WAVES][32];
+  __shared__ float red_s[SC_WAVES][32];
+
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int n = lane % 32, h = lane / 32;
+  const int bh = blockIdx.x / a.n_qgroups, qg = blockIdx.x % a.n_qgroups;
+  const int qb = qg * 32 + n;  // query block of this lane
+  const bool qok = qb < a.nQB;
+  const float* qm = a.q_mean + (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * D + h * HALF;
+  float qv[HALF];
+#pragma unroll
+  for (int z = 0; z < HALF / 4; ++z) {
+    const f32x4 x = qok ? *reinterpret_cast<const f32x4*>(qm + 4 * z) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int y = 0; y < 4; ++y) qv[4 * z + y] = x[y];
+  }
+  const float* kmb = a.k_mean + static_cast<size_t>(bh) * a.nKU * D + h * HALF;
+  float* srow = a.S + (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * a.nKU;
+  const int n_chunks = (a.nKU + 31) / 32;
+  const bool vec_ok = (a.nKU % 4) == 0;
+
+  float run_m = -INFINITY, run_s = 0.f;
+  for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
+    const int j0 = ch * 32;
+    const int ja = j0 + n;  // A-operand row (unit) of this lane
+    const bool aok = ja < a.nKU;
+    f32x16 acc = f32x16{};
+    const float* km = kmb + static_cast<size_t>(aok ? ja : 0) * D;
+#pragma unroll
+    for (int z = 0; z < HALF / 4; ++z) {
+      const f32x4 kv = aok ? *reinterpret_cast<const f32x4*>(km + 4 * z) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[y], qv[4 * z + y], acc, 0, 0, 0);
+    }
+    // register r holds unit j0 + 8 (r/4) + 4 h + r%4
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 8 * (r / 4) + 4 * h + (r % 4);
+      const bool valid = j < a.nKU && j * a.block_k < a.N;
+      acc[r] = valid ? acc[r] * a.sm_scale : -INFINITY;
+      lmax = fmaxf(lmax, acc[r]);
+    }
+    const float nm = fmaxf(run_m, lmax);
+    if (nm != -INFINITY) {
+      float s = run_m == -INFINITY ? 0.f : run_s * expf(run_m - nm);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = j0 + 8 * (r / 4) + 4 * h + (r % 4);
+        const float nj = static_cast<float>(max(0, min(a.block_k, a.N - j * a.block_k)));
+        if (acc[r] != -INFINITY) s += nj * expf(acc[r] - nm);
+      }
+      run_s = s;
+      run_m = nm;
+    }
+    if (qok) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j = j0 + 8 * g + 4 * h;
+        if (vec_ok && j + 3 < a.nKU) {
+          *reinterpret_cast<f32x4*>(srow + j) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+        } else {
+#pragma unroll
+          for (int y = 0; y < 4; ++y)
+            if (j + y < a.nKU) srow[j + y] = acc[4 * g + y];
+        }
+      }
+    }
+  }
+  // combine the two lane halves, then the waves
+  {
+    const float om = __shfl_xor(run_m, 32), os = __shfl_xor(run_s, 32);
+    const float nm = fmaxf(run_m, om);
+    float s = 0.f;
+    if (nm != -INFINITY) {
+      if (run_m != -INFINITY) s += run_s * expf(run_m - nm);
+      if (om != -INFINITY) s += os * expf(om - nm);
+    }
+    run_m = nm;
+    run_s = s;
+  }
+  if (h == 0) {
+    red_m[wave][n] = run_m;
+    red_s[wave][n] = run_s;
+  }
+  __threadfence();  // pass-1 logits are visible before they are read back
+  __syncthreads();
+  float Lm = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < SC_WAVES; ++x) Lm = fmaxf(Lm, red_m[x][n]);
+  float Z = 0.f;
+#pragma unroll
+  for (int x = 0; x < SC_WAVES; ++x)
+    if (red_m[x][n] != -INFINITY) Z += red_s[x][n] * expf(red_m[x][n] - Lm);
+  const float invZ = Z > 0.f ? 1.f / Z : 0.f;
+
+  if (!qok) return;
+  for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
+    const int j0 = ch * 32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int j = j0 + 8 * g + 4 * h;
+      if (vec_ok && j + 3 < a.nKU) {
+        f32x4 x = *reinterpret_cast<const f32x4*>(srow + j);
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int jj = j + y;
+          const float nj = static_cast<float>(max(0, min(a.block_k, a.N - jj * a.block_k)));
+          x[y] = nj > 0.f ? nj * expf(x[y] - Lm) * invZ : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(srow + j) = x;
+      } else {
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int jj = j + y;
+          if (jj < a.nKU) {
+            const float nj = static_cast<float>(max(0, min(a.block_k, a.N - jj * a.block_k)));
+            srow[jj] = nj > 0.f ? nj * expf(srow[jj] - Lm) * invZ : 0.f;
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, const int32_t* perm,
+                              float* q_mean, float* k_mean, hipStream_t s) {
+  MeansArgs a;
+  a.q = q;
+  a.k = k;
+  a.perm = perm;
+  a.q_mean = q_mean;
+  a.k_mean = k_mean;
+  a.N = g.N;
+  a.N_pad = g.N_pad;
+  a.block_q = g.block_q;
+  a.block_k = g.block_k;
+  a.nQB = g.nQB;
+  a.nKU = g.nKU;
+  a.n_bh = g.B * g.H;
+  const dim3 grid(a.n_bh * (g.nQB + g.nKU));
+  const bool p = perm != nullptr;
+#define BSA_MEANS(D, BF, P) hipLaunchKernelGGL((block_means_kernel<D, BF, P>), grid, dim3(MEAN_THREADS), 0, s, a)
+  if (g.d == 128) {
+    if (g.bf16) { if (p) BSA_MEANS(128, true, true); else BSA_MEANS(128, true, false); }
+    else { if (p) BSA_MEANS(128, false, true); else BSA_MEANS(128, false, false); }
+  } else {
+    if (g.bf16) { if (p) BSA_MEANS(64, true, true); else BSA_MEANS(64, true, false); }
+    else { if (p) BSA_MEANS(64, false, true); else BSA_MEANS(64, false, false); }
+  }
+#undef BSA_MEANS
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const Geometry& g, const float* q_mean, const float* k_mean, float* S,
+                         hipStream_t s) {
+  ScoreArgs a;
+  a.q_mean = q_mean;
+  a.k_mean = k_mean;
+  a.S = S;
+  a.N = g.N;
+  a.block_k = g.block_k;
+  a.nQB = g.nQB;
+  a.nKU = g.nKU;
+  a.n_qgroups = (g.nQB + 31) / 32;
+  a.sm_scale = g.sm_scale;
+  const dim3 grid(g.B * g.H * a.n_qgroups);
+  if (g.d == 128) hipLaunchKernelGGL((scores_kernel<128>), grid, dim3(64 * SC_WAVES), 0, s, a);
+  else hipLaunchKernelGGL((scores_kernel<64>), grid, dim3(64 * SC_WAVES), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

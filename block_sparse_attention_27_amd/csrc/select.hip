@@ -1,0 +1,350 @@
+// Block selection for gfx950: exact top-k set plus a fixed-size systematic
+// sample weighted by inverse inclusion probability, one workgroup per
+// (b, h, query block).
+//
+// What is computed (InstaGen, Abstract: exact set computed in full, the rest
+// represented by a sample drawn in proportion to estimated attention and
+// reweighted by inverse sampling probability, one sample per query cluster;
+// AB-Attention transcript: inclusion probabilities with certain inclusion for
+// the strongest blocks, a fixed number of distinct blocks, probability 1/4 ->
+// weight 4):
+//   1. exact set K = the k valid units with the largest score (ties: lower
+//      index; NaN/zero/negative scores count as 0, +inf as FLT_MAX);
+//   2. on the rest R, integer scores q_j = max(1, floor(s_j 2^(20 - e))) with
+//      e the binary exponent of max_R s; exact water-filling of
+//      pi_j = min(1, c q_j), sum_R pi_j = m; pi in 32-bit fixed point with
+//      floor(2^32 fl64((m-t) q_j) / fl64(Q_U)) and the integer shortfall paid
+//      as +1 to the first uncapped units, so sum_R pi_int = m 2^32 exactly;
+//   3. systematic sampling over R in index order from the offset
+//      u = Philox4x32-10((i, h, b, 0), seed) word 0;
+//   4. emit K ascending with w = 1, then sample slot s -> its unit with
+//      w = fp32(2^32 / pi_int).
+// Every sum is an integer sum, so the result is independent of reduction
+// order and bit-identical to the CPU definition. The only floating-point
+// operations are two correctly rounded fp64 divisions and one fp64 -> fp32
+// rounding.
+//
+// Layout: thread t owns the E consecutive units [t E, t E + E), so block-wide
+// exclusive scans give ranks in unit order directly.
+#include "bsa_internal.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr int SEL_THREADS = 256;
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int FS = 20;  // score quantisation bits
+
+struct SelectArgs {
+  const float* S;
+  int32_t* idx;
+  float* w;
+  int H, nQB, nKU, nV, k, m;
+  uint32_t seed_lo, seed_hi;
+};
+
+// Philox4x32-10 (Salmon et al., SC'11): word 0 of the output block.
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint32_t lo0 = M0 * c0, hi0 = __umulhi(M0, c0);
+    const uint32_t lo1 = M1 * c2, hi1 = __umulhi(M1, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return c0;
+}
+
+// NaN, zero and negatives -> 0; +inf -> FLT_MAX; other values keep their bits
+// (monotone in the value for non-negative floats).
+__device__ __forceinline__ uint32_t sanitize(uint32_t b) {
+  if (b >> 31) return 0u;
+  if ((b & 0x7F800000u) == 0x7F800000u) return (b & 0x007FFFFFu) ? 0u : 0x7F7FFFFFu;
+  return b;
+}
+
+// e such that the value of bits x (> 0, finite) is f 2^e with f in [0.5, 1).
+__device__ __forceinline__ int frexp_exp(uint32_t x) {
+  const int E = static_cast<int>(x >> 23);
+  if (E > 0) return E - 126;
+  const uint32_t mant = x & 0x007FFFFFu;
+  return (32 - __clz(mant)) - 149;
+}
+
+// floor(value(x) 2^(FS - e)), at least 1; exact integer arithmetic.
+__device__ __forceinline__ uint32_t quantise(uint32_t x, int e) {
+  if (x == 0u) return 1u;
+  const int E = static_cast<int>(x >> 23);
+  const uint64_t sig = E ? ((x & 0x007FFFFFu) | 0x00800000u) : (x & 0x007FFFFFu);
+  const int shift = (E ? E : 1) - 150 + FS - e;
+  uint64_t q;
+  if (shift >= 0) q = sig << shift;
+  else if (shift > -64) q = sig >> (-shift);
+  else q = 0;
+  return q > 0 ? static_cast<uint32_t>(q) : 1u;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* red) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  v = wave_sum(v);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  T t = 0;
+#pragma unroll
+  for (int x = 0; x < SEL_WAVES; ++x) t += red[x];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(v, off)));
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (int x = 0; x < SEL_WAVES; ++x) t = max(t, red[x]);
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix over threads in index order; `total` receives the block sum.
+__device__ __forceinline__ uint64_t block_exscan(uint64_t v, uint64_t* red, uint64_t& total) {
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  uint64_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  uint64_t before = 0, tot = 0;
+#pragma unroll
+  for (int z = 0; z < SEL_WAVES; ++z) {
+    const uint64_t r = red[z];
+    if (z < wave) before += r;
+    tot += r;
+  }
+  __syncthreads();
+  total = tot;
+  return before + x - v;
+}
+
+template <int E>
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
+  __shared__ uint32_t sbits[SEL_THREADS * E];
+  __shared__ uint64_t red64[SEL_WAVES];
+  __shared__ uint32_t red32[SEL_WAVES];
+
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  const int i = row % a.nQB, bh = row / a.nQB;
+  const int hd = bh % a.H, b = bh / a.H;
+  const float* srow = a.S + static_cast<size_t>(row) * a.nKU;
+  const int L = a.k + a.m;
+  int32_t* irow = a.idx + static_cast<size_t>(row) * L;
+  float* wrow = a.w + static_cast<size_t>(row) * L;
+
+  for (int x = tid; x < a.nV; x += SEL_THREADS) sbits[x] = __float_as_uint(srow[x]);
+  __syncthreads();
+
+  uint32_t key[E];
+  bool valid[E], inK[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = tid * E + e;
+    valid[e] = j < a.nV;
+    key[e] = valid[e] ? sanitize(sbits[j]) : 0u;
+    inK[e] = false;
+  }
+
+  // ---- 1. exact set: T = k-th largest key, ties by lower index ----
+  if (a.k > 0) {
+    uint32_t T = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) c += (valid[e] && key[e] >= cand) ? 1u : 0u;
+      if (block_sum(c, red32) >= static_cast<uint32_t>(a.k)) T = cand;
+    }
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gt += (valid[e] && key[e] > T) ? 1u : 0u;
+      eq += (valid[e] && key[e] == T) ? 1u : 0u;
+    }
+    const uint32_t need = static_cast<uint32_t>(a.k) - block_sum(gt, red32);
+    uint64_t eq_total;
+    uint32_t r = static_cast<uint32_t>(block_exscan(eq, red64, eq_total));
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!valid[e]) continue;
+      if (key[e] > T) {
+        inK[e] = true;
+      } else if (key[e] == T) {
+        inK[e] = r < need;
+        ++r;
+      }
+    }
+  }
+
+  bool inR[E], capped[E];
+  uint64_t pi[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    inR[e] = valid[e] && !inK[e];
+    capped[e] = false;
+    pi[e] = 0;
+  }
+
+  uint64_t delta = 0;
+  if (a.m > 0) {
+    // ---- 2a. quantised scores over R ----
+    uint32_t mx = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (inR[e]) mx = max(mx, key[e]);
+    mx = block_max(mx, red32);
+    uint32_t q[E];
+    const int ex = mx ? frexp_exp(mx) : 0;
+    uint64_t qsum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      q[e] = inR[e] ? (mx ? quantise(key[e], ex) : 1u) : 0u;
+      qsum += q[e];
+    }
+    uint64_t QU = block_sum(qsum, red64);
+
+    // ---- 2b. water-filling on exact integers ----
+    uint64_t t = 0;
+    while (true) {
+      const uint64_t mt = static_cast<uint64_t>(a.m) - t;
+      uint64_t packed = 0;  // (count << 40) | sum of q
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (inR[e] && !capped[e] && mt * q[e] >= QU) {
+          capped[e] = true;
+          packed += (1ull << 40) + q[e];
+        }
+      }
+      packed = block_sum(packed, red64);
+      const uint64_t cnt = packed >> 40;
+      if (cnt == 0) break;
+      t += cnt;
+      QU -= packed & ((1ull << 40) - 1);
+    }
+
+    // ---- 2c. fixed-point pi ----
+    const uint64_t mt = static_cast<uint64_t>(a.m) - t;
+    uint64_t usum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!inR[e]) continue;
+      if (capped[e]) {
+        pi[e] = 1ull << 32;
+      } else {
+        const double ratio = static_cast<double>(mt * q[e]) / static_cast<double>(QU);
+        pi[e] = static_cast<uint64_t>(ratio * 4294967296.0);
+        usum += pi[e];
+      }
+    }
+    delta = (mt << 32) - block_sum(usum, red64);
+  }
+
+  // ---- ranks in unit order: K (high word) and uncapped R (low word) ----
+  uint32_t nk = 0, nu = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    nk += inK[e] ? 1u : 0u;
+    nu += (inR[e] && !capped[e]) ? 1u : 0u;
+  }
+  uint64_t rk_total;
+  const uint64_t rk = block_exscan((static_cast<uint64_t>(nk) << 32) | nu, red64, rk_total);
+  uint32_t kpos = static_cast<uint32_t>(rk >> 32);
+  uint32_t upos = static_cast<uint32_t>(rk);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = tid * E + e;
+    if (inK[e]) {
+      irow[kpos] = j;
+      wrow[kpos] = 1.0f;
+      ++kpos;
+    }
+    if (a.m > 0 && inR[e] && !capped[e]) {
+      if (upos < delta) pi[e] += 1;
+      ++upos;
+    }
+  }
+
+  if (a.m > 0) {
+    // ---- 3. systematic sample over the cumulative pi axis ----
+    uint64_t psum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) psum += pi[e];
+    uint64_t ptotal;
+    uint64_t c = block_exscan(psum, red64, ptotal);
+    const uint64_t u = philox_word0(static_cast<uint32_t>(i), static_cast<uint32_t>(hd),
+                                    static_cast<uint32_t>(b), 0u, a.seed_lo, a.seed_hi);
+    auto below = [u](uint64_t x) -> uint64_t { return x > u ? ((x - u - 1) >> 32) + 1 : 0; };
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!inR[e]) continue;
+      const uint64_t c0 = c;
+      c += pi[e];
+      const uint64_t n0 = below(c0), n1 = below(c);
+      if (n1 > n0 && n0 < static_cast<uint64_t>(a.m)) {  // n0 < m always holds when sum pi = m 2^32
+        const int slot = a.k + static_cast<int>(n0);
+        irow[slot] = tid * E + e;
+        wrow[slot] = static_cast<float>(4294967296.0 / static_cast<double>(pi[e]));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const Geometry& g, int k_exact, int m_sample, const float* S, int32_t* idx,
+                         float* w, hipStream_t s) {
+  SelectArgs a;
+  a.S = S;
+  a.idx = idx;
+  a.w = w;
+  a.H = g.H;
+  a.nQB = g.nQB;
+  a.nKU = g.nKU;
+  a.nV = g.n_valid_units;
+  a.k = k_exact;
+  a.m = m_sample;
+  a.seed_lo = static_cast<uint32_t>(g.seed);
+  a.seed_hi = static_cast<uint32_t>(g.seed >> 32);
+  const dim3 grid(g.B * g.H * g.nQB), block(SEL_THREADS);
+  if (a.nV <= SEL_THREADS) hipLaunchKernelGGL((select_kernel<1>), grid, block, 0, s, a);
+  else if (a.nV <= 2 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<2>), grid, block, 0, s, a);
+  else if (a.nV <= 4 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<4>), grid, block, 0, s, a);
+  else if (a.nV <= 8 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<8>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((select_kernel<16>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

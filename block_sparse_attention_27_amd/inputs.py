@@ -33,8 +33,10 @@ head can be made alone.
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Iterable, Optional
 
 import numpy as np
@@ -144,10 +146,16 @@ WORKLOADS = {
 
 
 def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
-    """Round fp32 values to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    """Round finite fp32 values to bf16 (nearest, ties to even); returns the uint16 bit patterns.
+
+    The 32-bit sum cannot wrap: the largest finite pattern plus 0x8000 stays below 2^32.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def f32_from_bf16_bits(bits: np.ndarray) -> np.ndarray:
@@ -200,26 +208,27 @@ def generate(w: Workload, heads: Optional[Iterable[int]] = None) -> dict:
     k = np.zeros(shape, dtype=store)
     v = np.zeros(shape, dtype=store)
     inv_sqrt_d = np.float32(1.0 / math.sqrt(d))
-    for b in range(w.B):
-        for hi, h in enumerate(heads):
-            rng = np.random.default_rng([w.seed, 1, b, h])
-            mu = rng.standard_normal((w.clusters, d), dtype=np.float32) * np.float32(w.centroid_std)
-            base = mu[cid]
-            eq = rng.standard_normal((N, d), dtype=np.float32) * np.float32(w.noise_std)
-            qh = (base + eq) * inv_sqrt_d
-            del eq
-            ek = rng.standard_normal((N, d), dtype=np.float32) * np.float32(w.noise_std)
-            kh = (base + ek) * inv_sqrt_d
-            del ek, base
-            vh = rng.standard_normal((N, d), dtype=np.float32)
-            if bf16:
-                q[b, hi, :N] = bf16_bits_from_f32(qh)
-                k[b, hi, :N] = bf16_bits_from_f32(kh)
-                v[b, hi, :N] = bf16_bits_from_f32(vh)
-            else:
-                q[b, hi, :N] = qh
-                k[b, hi, :N] = kh
-                v[b, hi, :N] = vh
+
+    def one_head(job):
+        b, hi, h = job
+        rng = np.random.default_rng([w.seed, 1, b, h])
+        mu = rng.standard_normal((w.clusters, d), dtype=np.float32) * np.float32(w.centroid_std)
+        base = mu[cid]
+        out = []
+        for noisy in (True, True, False):  # Q, K share the centroid; V is pure noise
+            x = rng.standard_normal((N, d), dtype=np.float32)
+            if noisy:
+                x *= np.float32(w.noise_std)
+                x += base
+                x *= inv_sqrt_d
+            out.append(x)
+        for dst, x in zip((q, k, v), out):
+            dst[b, hi, :N] = bf16_bits_from_f32(x) if bf16 else x
+
+    jobs = [(b, hi, h) for b in range(w.B) for hi, h in enumerate(heads)]
+    workers = max(1, min(8, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one_head, jobs))
     perm = _permutation(w, cid) if w.permute else None
     return {"q": q, "k": k, "v": v, "perm": perm, "heads": heads}
 

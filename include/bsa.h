@@ -1,0 +1,165 @@
+/*
+ * bsa.h -- weighted dynamic block-sparse attention for video DiTs on AMD
+ * Instinct MI355X (gfx950). C ABI of libbsa.so.
+ *
+ * The method (InstaGen, "Group-Shared Importance Sampling for Fast Video
+ * Generation", Abstract; AB-Attention, "Accurate Block Attention", Abstract
+ * and the transcript's sections on inclusion-probability sampling and the
+ * tiled kernel): every query block scores the key blocks from block summaries,
+ * keeps the top-scoring ones as an exact set, draws a fixed-size sample of
+ * the rest in proportion to the estimated attention, and runs one sparse
+ * attention pass in which every sampled block is reweighted by the inverse of
+ * its inclusion probability in both the softmax numerator and denominator.
+ *
+ * Pipeline: bsa_score -> bsa_select -> bsa_attend. bsa_attend_dense is plain
+ * dense attention built on the same tiling, for timing and checking.
+ *
+ * Conventions shared by every call
+ *   Layout     Q, K, V and out are contiguous row-major [B][H][N_pad][d]
+ *              (element type `dtype`); S is [B][H][nQB][nKU] fp32; idx and w
+ *              are [B][H][nQB][k_exact + m_sample] (int32 / fp32); lse is
+ *              [B][H][N_pad] fp32. nQB = N_pad / block_q, nKU = N_pad / block_k.
+ *   Validity   Rows r < N are tokens, rows N..N_pad-1 are padding. Padding rows
+ *              of Q, K and V are never read (their contents do not matter);
+ *              padding rows of out are written as zeros and their lse as -inf.
+ *              Key unit j holds keys [j*block_k, (j+1)*block_k) and is valid
+ *              when j*block_k < N; a partly filled tail unit uses only its
+ *              keys below N.
+ *   Permutation perm, when not NULL, is int32[N_pad] on the device: the
+ *              computation runs on the gathered rows X'[r] = X[perm[r]] for
+ *              Q, K and V alike, and row r of the result is written to row
+ *              perm[r] of out (and lse). perm must map 0..N-1 onto 0..N-1;
+ *              entries r >= N are not read. An entry outside [0, N_pad) makes
+ *              that row read as zeros (no out-of-bounds access).
+ *   Memory     All array arguments are device pointers owned by the caller;
+ *              Q/K/V/out must be 16-byte aligned, the others 4-byte aligned.
+ *              The library allocates nothing, keeps no state between calls and
+ *              may be called from several host threads on different streams.
+ *   Execution  Every call only enqueues work on `stream` and returns; the
+ *              caller synchronises. Calls on one stream run in order.
+ *   Errors     Invalid arguments return BSA_ERR_INVALID_ARG before anything is
+ *              launched; shapes the kernels do not implement return
+ *              BSA_ERR_UNSUPPORTED; a failed launch returns BSA_ERR_HIP.
+ *              Faults inside a kernel surface at the caller's synchronisation.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_ABI_VERSION 1
+
+typedef enum bsa_status {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1,
+  BSA_ERR_UNSUPPORTED = 2,
+  BSA_ERR_HIP = 3
+} bsa_status;
+
+typedef enum bsa_dtype {
+  BSA_BF16 = 0, /* bfloat16 Q/K/V/out, bf16 MFMA with fp32 accumulation */
+  BSA_FP32 = 1  /* float Q/K/V/out, fp32 arithmetic throughout */
+} bsa_dtype;
+
+/* The problem statement shared by all calls (InstaGen, Abstract: Q/K/V, a
+ * block size, an exact-set size, a sample size and a random seed). */
+typedef struct bsa_problem {
+  int32_t B, H;       /* batch, heads (>= 1) */
+  int32_t N;          /* valid tokens, 1 <= N <= N_pad */
+  int32_t N_pad;      /* padded rows; a multiple of block_q and of block_k */
+  int32_t d;          /* head dimension: 64 or 128 */
+  int32_t block_q;    /* query-block rows: 64 or 128 */
+  int32_t block_k;    /* key-unit rows: 32, 64 or 128 (4, 2 or 1 per 128-key tile) */
+  int32_t k_exact;    /* exact-set size k >= 0 */
+  int32_t m_sample;   /* sample size m >= 0; 1 <= k+m <= number of valid units */
+  int32_t dtype;      /* bsa_dtype */
+  uint64_t seed;      /* sampler seed (Philox4x32-10 key) */
+  float sm_scale;     /* logit = sm_scale * <q, k>; finite and > 0 */
+  int32_t reserved;   /* must be 0 */
+} bsa_problem;
+
+/* Returns BSA_ABI_VERSION. */
+int32_t bsa_abi_version(void);
+
+/* Static text for a bsa_status value (never NULL). */
+const char* bsa_status_string(int32_t status);
+
+/*
+ * bsa_score -- block summaries and estimated attention per key unit.
+ * (AB-Attention, Abstract: blocks scored from coarse summaries; InstaGen,
+ * Abstract: sample drawn in proportion to estimated attention.)
+ *
+ *   q_mean[b,h,i,:] = mean of the valid rows of query block i      (fp32, out)
+ *   k_mean[b,h,j,:] = mean of the n_j valid keys of unit j          (fp32, out)
+ *   S[b,h,i,j] = n_j exp(l_ij) / sum_{valid j'} n_j' exp(l_ij'),
+ *       l_ij = sm_scale <q_mean_i, k_mean_j>;  S = 0 for invalid units.
+ * A query block with no valid row has q_mean = 0. Uses q, k (dtype), perm
+ * (optional, see above). q_mean is [B][H][nQB][d], k_mean [B][H][nKU][d];
+ * both are written (the caller owns them; 16-byte aligned).
+ */
+bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const int32_t* perm,
+                     float* S, float* q_mean, float* k_mean, hipStream_t stream);
+
+/*
+ * bsa_select -- exact set plus fixed-size weighted sample, per (b, h, i).
+ * (InstaGen, Abstract: exact set plus a weighted sample, one sample shared by
+ * a query cluster; AB-Attention transcript: inclusion probabilities, a fixed
+ * number of distinct blocks, and 1/pi weights -- probability 1/4 counts 4x.)
+ *
+ * For each row of S (only the valid units 0..ceil(N/block_k)-1 are read):
+ *   1. exact set: the k valid units with the largest score (ties: lower
+ *      index); NaN, zero and negative scores count as 0, +inf as FLT_MAX;
+ *   2. the other valid units R get inclusion probabilities
+ *      pi_j = min(1, c s_j) with sum_R pi_j = m, computed bit-reproducibly:
+ *      scores quantised to 20-bit integers relative to the row maximum
+ *      (minimum 1), exact integer water-filling for c, pi in 32-bit fixed
+ *      point summing to exactly m * 2^32;
+ *   3. systematic sampling over R in ascending unit order with offset
+ *      u = word 0 of Philox4x32-10(counter = (i, h, b, 0),
+ *      key = (seed & 0xffffffff, seed >> 32)) gives exactly m distinct units.
+ * Output row: idx[0..k) = exact set ascending, w = 1; idx[k + s] = the unit
+ * drawn by the s-th sample point, w = fp32(2^32 / pi_int) (1 for units with
+ * pi = 1). Results are bit-identical to the reference definition for any
+ * input S. Needs ceil(N/block_k) <= 4096.
+ */
+bsa_status bsa_select(const bsa_problem* p, const float* S, int32_t* idx, float* w,
+                      hipStream_t stream);
+
+/*
+ * bsa_attend -- one weighted block-sparse attention pass.
+ * (AB-Attention, Abstract and transcript: the weights enter numerator and
+ * denominator alike -- equivalently the sampled logits are shifted by ln w
+ * before the softmax -- and small key blocks are gathered into full
+ * matrix-core tiles; InstaGen, Abstract: sampled keys kept block-shaped.)
+ *
+ * For every valid query row r of block i, over the list entries (j, w_j) of
+ * that block and the valid keys t of unit j, with a_rt = sm_scale <q_r, k_t>:
+ *   out_r = sum_j w_j sum_t exp(a_rt) v_t / sum_j w_j sum_t exp(a_rt)
+ *   lse_r = ln(sum_j w_j sum_t exp(a_rt))
+ * The list is used as given (a repeated entry counts twice); entries with an
+ * index outside [0, nKU) or a weight that is not > 0 contribute nothing.
+ * idx/w may come from bsa_select or from the caller (e.g. a plan reused across
+ * denoising steps). lse may be NULL. out has the element type `dtype`.
+ */
+bsa_status bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* v,
+                      const int32_t* perm, const int32_t* idx, const float* w, void* out,
+                      float* lse, hipStream_t stream);
+
+/*
+ * bsa_attend_dense -- masked softmax(sm_scale Q K^T) V over the N valid keys,
+ * same layouts, permutation and outputs as bsa_attend (k_exact, m_sample and
+ * seed are ignored). The timing and accuracy reference for the sparse pass.
+ */
+bsa_status bsa_attend_dense(const bsa_problem* p, const void* q, const void* k, const void* v,
+                            const int32_t* perm, void* out, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

@@ -1,0 +1,199 @@
+"""GPU parity: every HIP kernel against the CPU oracle on the same seeded inputs.
+
+Bars (written here, applied per check):
+  selection  bit-exact idx and bit-exact fp32 w, fed the same fp32 S;
+  scores     |S_gpu - S_ref| <= 1e-3 S_ref + 1e-12 max_j S_ref elementwise;
+  attention  relative L2 <= 2e-3 and max |diff| <= 1e-2 over the checked rows,
+             fed the same idx/w; lse within 2e-3 absolute.
+Small workloads are compared whole; the full-size layers are compared on
+sampled (head, query block) pairs that include the first and the padded last
+block, in the launch configuration the bench times.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_27_amd as bsa
+import oracle
+from block_sparse_attention_27_amd.inputs import WORKLOADS, generate
+from gpu_util import to_device, to_f64, host_f64, rel_l2, print_case
+
+pytestmark = pytest.mark.gpu
+
+SCORE_RTOL = 1e-3
+OUT_REL_L2 = 2e-3
+OUT_MAX_ABS = 1e-2
+LSE_ABS = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bsa.load_library()
+
+
+@functools.lru_cache(maxsize=2)
+def workload_data(name):
+    w = WORKLOADS[name]
+    g = generate(w)
+    dev = {k: to_device(g[k]) for k in ("q", "k", "v")}
+    dev["perm"] = torch.from_numpy(g["perm"]).cuda() if g["perm"] is not None else None
+    return w, g, dev
+
+
+def _sample_blocks(w, n_heads, n_blocks, seed=0):
+    rng = np.random.default_rng(seed)
+    heads = sorted(set([0, w.H - 1] + rng.integers(0, w.H, n_heads).tolist()))[:max(2, n_heads)]
+    blocks = sorted(set([0, w.n_qblocks - 1] + rng.integers(0, w.n_qblocks, n_blocks).tolist()))
+    return heads, blocks
+
+
+def _head(x, h):
+    return x[:, h:h + 1]
+
+
+def check_scores(w, g, S_gpu, heads):
+    for h in heads:
+        q = host_f64(_head(g["q"], h)); k = host_f64(_head(g["k"], h))
+        S_ref, qb, kb = oracle.score(q, k, w.N, w.block_q, w.block_k, w.sm_scale, g["perm"])
+        got = S_gpu[:, h:h + 1].cpu().numpy().astype(np.float64)
+        ref = S_ref.astype(np.float64)
+        tol = SCORE_RTOL * ref + 1e-12 * ref.max(axis=-1, keepdims=True)
+        bad = np.abs(got - ref) > tol
+        assert not bad.any(), (f"head {h}: {bad.sum()} scores out of tolerance, worst rel "
+                               f"{np.max(np.abs(got - ref) / np.maximum(ref, 1e-30)):.3e}")
+
+
+def check_selection(w, S_gpu, idx_gpu, w_gpu, rows, seed):
+    S = S_gpu.cpu().numpy()
+    idx = idx_gpu.cpu().numpy(); wt = w_gpu.cpu().numpy()
+    for (b, h, i), (ri, rw) in zip(rows, oracle.select(S, w.N, w.block_k, w.k_exact, w.m_sample, seed,
+                                                        rows=rows)):
+        assert np.array_equal(idx[b, h, i], ri), (b, h, i, idx[b, h, i], ri)
+        assert np.array_equal(wt[b, h, i].view(np.uint32), rw.view(np.uint32)), (b, h, i)
+
+
+def check_attention(w, g, out_gpu, lse_gpu, idx, wt, pairs, dense=False):
+    perm = g["perm"]
+    out = out_gpu
+    errs = []
+    for h, blocks in pairs.items():
+        q = host_f64(_head(g["q"], h)); k = host_f64(_head(g["k"], h)); v = host_f64(_head(g["v"], h))
+        tri = [(0, 0, i) for i in blocks]
+        if dense:
+            ref = oracle.attend_dense(q, k, v, w.N, w.sm_scale, perm, blocks=tri, block_q=w.block_q)
+        else:
+            ref = oracle.attend(q, k, v, w.N, w.block_q, w.block_k, w.sm_scale,
+                                idx[:, h:h + 1], wt[:, h:h + 1], perm, blocks=tri)
+        for i, (o_ref, l_ref) in zip(blocks, ref):
+            rows = np.arange(i * w.block_q, (i + 1) * w.block_q)
+            orows = np.where(rows < w.N, perm[rows] if perm is not None else rows, rows)
+            got = to_f64(out[0, h, torch.from_numpy(orows).cuda()])
+            errs.append((got, o_ref))
+            if lse_gpu is not None:
+                gl = lse_gpu[0, h, torch.from_numpy(orows).cuda()].cpu().numpy().astype(np.float64)
+                ok = rows < w.N
+                assert np.all(np.isneginf(gl[~ok]))
+                assert np.max(np.abs(gl[ok] - l_ref[ok]), initial=0) < LSE_ABS, (h, i)
+            assert np.all(got[rows >= w.N] == 0)
+    got = np.concatenate([e[0] for e in errs]); ref = np.concatenate([e[1] for e in errs])
+    r, m = rel_l2(got, ref), float(np.max(np.abs(got - ref)))
+    print_case(f"  rel_l2={r:.3e} max_abs={m:.3e}")
+    assert r <= OUT_REL_L2 and m <= OUT_MAX_ABS, (r, m)
+
+
+# ------------------------------------------------------------------ tiny (fp32)
+
+def test_tiny_fp32_end_to_end():
+    print_case("tiny fp32: score, select, attend, dense vs oracle (whole tensors)")
+    w, g, dev = workload_data("tiny")
+    p = bsa.problem_for(w)
+    S, qm, km = bsa.score(p, dev["q"], dev["k"])
+    idx, wt = bsa.select(p, S)
+    out, lse = bsa.attend(p, dev["q"], dev["k"], dev["v"], idx, wt, with_lse=True)
+    outd, lsed = bsa.attend_dense(p, dev["q"], dev["k"], dev["v"], with_lse=True)
+    torch.cuda.synchronize()
+    q, k, v = (host_f64(g[x]) for x in ("q", "k", "v"))
+    S_ref, qb, kb = oracle.score(q, k, w.N, w.block_q, w.block_k, w.sm_scale)
+    assert rel_l2(qm.cpu().numpy(), qb) < 1e-6 and rel_l2(km.cpu().numpy(), kb) < 1e-6
+    check_scores(w, g, S, [0])
+    i_ref, w_ref = oracle.select(S.cpu().numpy(), w.N, w.block_k, w.k_exact, w.m_sample, w.select_seed)
+    assert np.array_equal(idx.cpu().numpy(), i_ref)
+    assert np.array_equal(wt.cpu().numpy().view(np.uint32), w_ref.view(np.uint32))
+    O_ref, L_ref = oracle.attend(q, k, v, w.N, w.block_q, w.block_k, w.sm_scale, i_ref, w_ref)
+    O = out.cpu().numpy().astype(np.float64)
+    assert rel_l2(O, O_ref) < 1e-5 and np.max(np.abs(O - O_ref)) < 1e-5
+    assert np.max(np.abs(lse.cpu().numpy() - L_ref)) < 1e-5
+    Od_ref, Ld_ref = oracle.attend_dense(q, k, v, w.N, w.sm_scale)
+    assert rel_l2(outd.cpu().numpy(), Od_ref) < 1e-5
+    assert np.max(np.abs(lsed.cpu().numpy() - Ld_ref)) < 1e-5
+
+
+# ------------------------------------------------------------- full-size layers
+
+LAYERS = {
+    # name: (heads checked for S, (heads, blocks) for attention, rows for selection)
+    "wan13b": (2, (2, 8), 400),
+    "wan14b_720p": (2, (2, 6), 300),
+    "hunyuan": (1, (2, 4), 80),
+}
+
+
+@pytest.mark.parametrize("name", list(LAYERS))
+def test_layer_score_select_attend(name):
+    print_case(f"{name}: generating inputs")
+    w, g, dev = workload_data(name)
+    n_s_heads, (n_a_heads, n_a_blocks), n_rows = LAYERS[name]
+    p = bsa.problem_for(w)
+    print_case(f"{name}: bsa_score/select/attend/attend_dense on the GPU")
+    S, qm, km = bsa.score(p, dev["q"], dev["k"], dev["perm"])
+    idx, wt = bsa.select(p, S)
+    out, lse = bsa.attend(p, dev["q"], dev["k"], dev["v"], idx, wt, dev["perm"], with_lse=True)
+    torch.cuda.synchronize()
+
+    print_case(f"{name}: scores vs oracle")
+    check_scores(w, g, S, list(range(n_s_heads)))
+
+    print_case(f"{name}: selection bit-exactness on {n_rows} sampled rows")
+    rng = np.random.default_rng(1)
+    rows = [(0, int(rng.integers(0, w.H)), int(rng.integers(0, w.n_qblocks))) for _ in range(n_rows)]
+    rows += [(0, 0, 0), (0, w.H - 1, w.n_qblocks - 1)]
+    check_selection(w, S, idx, wt, rows, w.select_seed)
+
+    print_case(f"{name}: attention vs oracle with the same lists")
+    heads, blocks = _sample_blocks(w, n_a_heads, n_a_blocks)
+    idx_h, wt_h = idx.cpu().numpy(), wt.cpu().numpy()
+    check_attention(w, g, out, lse, idx_h, wt_h, {h: blocks for h in heads})
+    del out, lse
+
+
+@pytest.mark.parametrize("name", ["wan13b", "hunyuan"])
+def test_layer_dense(name):
+    print_case(f"{name}: bsa_attend_dense vs oracle")
+    w, g, dev = workload_data(name)
+    p = bsa.problem_for(w)
+    out, lse = bsa.attend_dense(p, dev["q"], dev["k"], dev["v"], dev["perm"], with_lse=True)
+    torch.cuda.synchronize()
+    heads, blocks = _sample_blocks(w, 1, 3, seed=2)
+    check_attention(w, g, out, lse, None, None, {h: blocks for h in heads}, dense=True)
+
+
+def test_480p_temperature_sweep_selection_and_scores():
+    base = WORKLOADS["wan14b_480p"].replace(H=4)
+    for tau in (0.5, 1.0, 2.0):
+        w = base.replace(temperature=tau)
+        print_case(f"480p-shaped, 4 heads, temperature {tau}")
+        g = generate(w)
+        q, k, v = (to_device(g[x]) for x in ("q", "k", "v"))
+        p = bsa.problem_for(w)
+        S, _, _ = bsa.score(p, q, k)
+        idx, wt = bsa.select(p, S)
+        out = bsa.attend(p, q, k, v, idx, wt)
+        torch.cuda.synchronize()
+        check_scores(w, g, S, [0, 3])
+        rows = [(0, h, i) for h in range(4) for i in range(0, w.n_qblocks, 7)]
+        check_selection(w, S, idx, wt, rows, w.select_seed)
+        check_attention(w, g, out, None, idx.cpu().numpy(), wt.cpu().numpy(), {1: [0, 100, 255]})
