@@ -135,13 +135,14 @@ def main(argv=None):
 
     q, k, v = dev(g["q"]), dev(g["k"]), dev(g["v"])
     perm = torch.from_numpy(g["perm"]).cuda() if g["perm"] is not None else None
-    p = bsa.problem_for(w)
+    p = bsa.problem_for(w, out_fp32=1)   # the parity-checked variant: fp32 output
+    p16 = bsa.problem_for(w)             # same kernel, bf16 output (RNE of the fp32 result)
     S = torch.empty((w.B, w.H, w.n_qblocks, w.n_units), dtype=torch.float32, device="cuda")
     qm = torch.empty((w.B, w.H, w.n_qblocks, w.d), dtype=torch.float32, device="cuda")
     km = torch.empty((w.B, w.H, w.n_units, w.d), dtype=torch.float32, device="cuda")
     idx = torch.empty((w.B, w.H, w.n_qblocks, w.list_len), dtype=torch.int32, device="cuda")
     wt = torch.empty((w.B, w.H, w.n_qblocks, w.list_len), dtype=torch.float32, device="cuda")
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -171,10 +172,21 @@ def main(argv=None):
     t_attend = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
     t_pass = statistics.mean(e[0].elapsed_time(e[3]) for e in evs)
 
+    # bsa_attend with a bf16 output, same lists
+    out16 = torch.empty_like(q)
+    be = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
+    for e in be:
+        e[0].record(stream)
+        bsa.bsa_attend(p16, q, k, v, perm, idx, wt, out16, None)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t_attend16 = statistics.mean(e[0].elapsed_time(e[1]) for e in be)
+    del out16
+
     t_dense = None
     if not args.no_dense:
         _log("timing the dense kernel")
-        outd = torch.empty_like(q)
+        outd = torch.empty(q.shape, dtype=torch.float32, device="cuda")
         for _ in range(2):
             bsa.bsa_attend_dense(p, q, k, v, perm, outd, None)
         n_dense = max(3, min(args.steps, 10))
@@ -219,6 +231,7 @@ def main(argv=None):
         "t_score_ms": round(t_score, 4),
         "t_select_ms": round(t_select, 4),
         "t_attend_ms": round(t_attend, 4),
+        "t_attend_bf16_out_ms": round(t_attend16, 4),
         "t_dense_ms": None if t_dense is None else round(t_dense, 4),
         "score_select_share": round((t_score + t_select) / t_pass, 4),
         "executed_tflops": round(ach, 1),

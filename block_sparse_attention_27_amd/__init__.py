@@ -24,7 +24,7 @@ from typing import Optional
 from .inputs import Workload
 
 __all__ = [
-    "Problem", "BsaError", "load_library", "library_path", "problem_for",
+    "Problem", "BsaError", "load_library", "library_path", "problem_for", "out_dtype",
     "bsa_score", "bsa_select", "bsa_attend", "bsa_attend_dense",
     "score", "select", "attend", "attend_dense", "sparse_attention",
     "BSA_OK", "BSA_ERR_INVALID_ARG", "BSA_ERR_UNSUPPORTED", "BSA_ERR_HIP", "BSA_BF16", "BSA_FP32",
@@ -47,8 +47,8 @@ class Problem(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
         ("N_pad", ctypes.c_int32), ("d", ctypes.c_int32), ("block_q", ctypes.c_int32),
         ("block_k", ctypes.c_int32), ("k_exact", ctypes.c_int32), ("m_sample", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("seed", ctypes.c_uint64), ("sm_scale", ctypes.c_float),
-        ("reserved", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("seed", ctypes.c_uint64), ("sm_scale", ctypes.c_float),
     ]
 
     @property
@@ -112,7 +112,7 @@ def problem_for(w: Workload, seed: Optional[int] = None, **overrides) -> Problem
     f = dict(B=w.B, H=w.H, N=w.N, N_pad=w.N_pad, d=w.d, block_q=w.block_q, block_k=w.block_k,
              k_exact=w.k_exact, m_sample=w.m_sample,
              dtype=BSA_BF16 if w.dtype == "bf16" else BSA_FP32,
-             seed=w.select_seed if seed is None else seed, sm_scale=w.sm_scale, reserved=0)
+             out_fp32=0, seed=w.select_seed if seed is None else seed, sm_scale=w.sm_scale, reserved=0)
     f.update(overrides)
     return Problem(**f)
 
@@ -143,6 +143,12 @@ def _check(call: str, status: int):
 def _elem_dtype(p: Problem):
     import torch
     return torch.bfloat16 if p.dtype == BSA_BF16 else torch.float32
+
+
+def out_dtype(p: Problem):
+    """Element type of the attention output for this problem."""
+    import torch
+    return torch.bfloat16 if (p.dtype == BSA_BF16 and not p.out_fp32) else torch.float32
 
 
 def _expect(name, t, shape, dtype):
@@ -178,8 +184,9 @@ def bsa_attend(p: Problem, q, k, v, perm, idx, w, out, lse=None, stream=None):
     import torch
     et = _elem_dtype(p)
     qkv_shape = (p.B, p.H, p.N_pad, p.d)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+    for name, t in (("q", q), ("k", k), ("v", v)):
         _expect(name, t, qkv_shape, et)
+    _expect("out", out, qkv_shape, out_dtype(p))
     _expect("perm", perm, (p.N_pad,), torch.int32)
     _expect("idx", idx, (p.B, p.H, p.nQB, p.L), torch.int32)
     _expect("w", w, (p.B, p.H, p.nQB, p.L), torch.float32)
@@ -193,8 +200,9 @@ def bsa_attend_dense(p: Problem, q, k, v, perm, out, lse=None, stream=None):
     import torch
     et = _elem_dtype(p)
     qkv_shape = (p.B, p.H, p.N_pad, p.d)
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+    for name, t in (("q", q), ("k", k), ("v", v)):
         _expect(name, t, qkv_shape, et)
+    _expect("out", out, qkv_shape, out_dtype(p))
     _expect("perm", perm, (p.N_pad,), torch.int32)
     _expect("lse", lse, (p.B, p.H, p.N_pad), torch.float32)
     _check("bsa_attend_dense", load_library().bsa_attend_dense(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
@@ -227,7 +235,7 @@ def select(p: Problem, S, stream=None):
 def attend(p: Problem, q, k, v, idx, w, perm=None, with_lse=False, stream=None):
     """Returns out (and lse when ``with_lse``)."""
     import torch
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=out_dtype(p), device=q.device)
     lse = torch.empty((p.B, p.H, p.N_pad), dtype=torch.float32, device=q.device) if with_lse else None
     bsa_attend(p, q, k, v, perm, idx, w, out, lse, stream)
     return (out, lse) if with_lse else out
@@ -235,7 +243,7 @@ def attend(p: Problem, q, k, v, idx, w, perm=None, with_lse=False, stream=None):
 
 def attend_dense(p: Problem, q, k, v, perm=None, with_lse=False, stream=None):
     import torch
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=out_dtype(p), device=q.device)
     lse = torch.empty((p.B, p.H, p.N_pad), dtype=torch.float32, device=q.device) if with_lse else None
     bsa_attend_dense(p, q, k, v, perm, out, lse, stream)
     return (out, lse) if with_lse else out

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbsa.so")
-SOURCES = ["bsa_api.hip", "score.hip", "select.hip", "attend_bf16.hip", "attend_fp32.hip"]
+SOURCES = ["bsa_api.hip", "score.hip", "select.hip", "attend_bf16_d128.hip", "attend_bf16_d64.hip",
+           "attend_fp32.hip"]
 
 # Packed-fp32 instructions stay off (hipcc may otherwise form v_pk_* from float code).
 HIPFLAGS = [
@@ -28,7 +29,7 @@ def _hipcc() -> str:
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
+def build(verbose: bool = False, jobs: int = 6) -> str:
     """Compile every source and link libbsa.so; returns the library path."""
     obj_dir = os.path.join(PKG, "_build")
     os.makedirs(obj_dir, exist_ok=True)

@@ -19,12 +19,14 @@
 // using v_mfma_f32_32x32x16_bf16. In the S^T orientation a lane holds one
 // query row, so row max and row sum never leave the lane except for one
 // exchange between the two 32-lane halves per tile.
+#pragma once
+
 #include "bsa_internal.hpp"
 
 #include <math.h>
 
 namespace bsa {
-namespace {
+namespace attend_bf16_impl {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -40,7 +42,7 @@ struct AttendArgs {
   const int32_t* perm;
   const int32_t* idx;
   const float* w;
-  uint16_t* out;
+  void* out;
   float* lse;
   int H, N, N_pad, nQB, nKU, L, n_tiles, n_wg;
   float c;  // sm_scale * log2(e)
@@ -203,7 +205,7 @@ __device__ __forceinline__ void stage_tile(const AttendArgs& a, const uint16_t* 
   }
 }
 
-template <int D, int BQ, int BK, bool DENSE, bool PERM>
+template <int D, int BQ, int BK, bool DENSE, bool PERM, bool OUT32>
 __global__ __launch_bounds__(BQ * 2, 2) void attend_bf16_kernel(AttendArgs a) {
   constexpr int NW = BQ / 32;
   constexpr int NT = 64 * NW;
@@ -334,73 +336,76 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_bf16_kernel(AttendArgs a) {
 
   // ---- epilogue: O^T register r of d-tile dt holds d = 32 dt + 8 (r/4) + 4 h + r%4 ----
   const float l_tot = l_part + __shfl_xor(l_part, 32);
-  const size_t out_bh = bh_off;
+  bool ok = true;
+  int orow = qrow;
+  float inv = 0.f;
   if (qrow < a.N) {
-    bool ok = true;
-    const int orow = gather_row<PERM>(a, qrow, ok);
-    if (ok) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      uint16_t* op = a.out + out_bh + static_cast<size_t>(orow) * D;
+    orow = gather_row<PERM>(a, qrow, ok);
+    inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  }
+  if (ok) {  // rows >= N (inv = 0) are written as zeros
+    const size_t obase = bh_off + static_cast<size_t>(orow) * D;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
+    for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * dt + 8 * g + 4 * h;
+        float x[4];
+#pragma unroll
+        for (int z = 0; z < 4; ++z) x[z] = o[dt][4 * g + z] * inv;
+        if constexpr (OUT32) {
+          float* op = static_cast<float*>(a.out) + obase + col;
+          *reinterpret_cast<float4*>(op) = make_float4(x[0], x[1], x[2], x[3]);
+        } else {
           uint32_t pk[2];
 #pragma unroll
           for (int z = 0; z < 2; ++z) {
-            const __bf16 lo = static_cast<__bf16>(o[dt][4 * g + 2 * z] * inv);
-            const __bf16 hi = static_cast<__bf16>(o[dt][4 * g + 2 * z + 1] * inv);
+            const __bf16 lo = static_cast<__bf16>(x[2 * z]);
+            const __bf16 hi = static_cast<__bf16>(x[2 * z + 1]);
             pk[z] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                     (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
           }
-          *reinterpret_cast<uint2*>(op + 32 * dt + 8 * g + 4 * h) = make_uint2(pk[0], pk[1]);
+          uint16_t* op = static_cast<uint16_t*>(a.out) + obase + col;
+          *reinterpret_cast<uint2*>(op) = make_uint2(pk[0], pk[1]);
         }
       }
-      if (a.lse != nullptr && h == 0) {
-        a.lse[static_cast<size_t>(bh) * a.N_pad + orow] =
-            l_tot > 0.f ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
-      }
     }
-  } else {
-    uint16_t* op = a.out + out_bh + static_cast<size_t>(qrow) * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) *reinterpret_cast<uint2*>(op + 32 * dt + 8 * g + 4 * h) = make_uint2(0u, 0u);
-    if (a.lse != nullptr && h == 0) a.lse[static_cast<size_t>(bh) * a.N_pad + qrow] = -INFINITY;
+    if (a.lse != nullptr && h == 0) {
+      a.lse[static_cast<size_t>(bh) * a.N_pad + orow] =
+          (qrow < a.N && l_tot > 0.f) ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+    }
   }
 }
 
-template <int D, int BQ, int BK, bool DENSE, bool PERM>
+template <int D, int BQ, int BK, bool DENSE, bool PERM, bool OUT32>
 hipError_t launch_one(const AttendArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attend_bf16_kernel<D, BQ, BK, DENSE, PERM>), dim3(a.n_wg), dim3(BQ * 2), 0, s, a);
+  hipLaunchKernelGGL((attend_bf16_kernel<D, BQ, BK, DENSE, PERM, OUT32>), dim3(a.n_wg), dim3(BQ * 2), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, int BQ, bool DENSE, bool PERM>
+template <int D, int BQ, bool DENSE, bool PERM, bool OUT32>
 hipError_t dispatch_bk(const AttendArgs& a, int bk, hipStream_t s) {
   if constexpr (DENSE) {
-    return launch_one<D, BQ, 128, true, PERM>(a, s);
+    return launch_one<D, BQ, 128, true, PERM, OUT32>(a, s);
   } else {
     switch (bk) {
-      case 32: return launch_one<D, BQ, 32, false, PERM>(a, s);
-      case 64: return launch_one<D, BQ, 64, false, PERM>(a, s);
-      default: return launch_one<D, BQ, 128, false, PERM>(a, s);
+      case 32: return launch_one<D, BQ, 32, false, PERM, OUT32>(a, s);
+      case 64: return launch_one<D, BQ, 64, false, PERM, OUT32>(a, s);
+      default: return launch_one<D, BQ, 128, false, PERM, OUT32>(a, s);
     }
   }
 }
 
-template <int D, int BQ>
+template <int D, int BQ, bool OUT32>
 hipError_t dispatch_mode(const AttendArgs& a, int bk, bool dense, bool perm, hipStream_t s) {
-  if (dense) return perm ? dispatch_bk<D, BQ, true, true>(a, bk, s) : dispatch_bk<D, BQ, true, false>(a, bk, s);
-  return perm ? dispatch_bk<D, BQ, false, true>(a, bk, s) : dispatch_bk<D, BQ, false, false>(a, bk, s);
+  if (dense) return perm ? dispatch_bk<D, BQ, true, true, OUT32>(a, bk, s) : dispatch_bk<D, BQ, true, false, OUT32>(a, bk, s);
+  return perm ? dispatch_bk<D, BQ, false, true, OUT32>(a, bk, s) : dispatch_bk<D, BQ, false, false, OUT32>(a, bk, s);
 }
 
-}  // namespace
-
-hipError_t launch_attend_bf16(const Geometry& g, const void* q, const void* k, const void* v,
-                              const int32_t* perm, const int32_t* idx, const float* w, void* out,
-                              float* lse, hipStream_t s) {
+// Launch for one head dimension D (one translation unit per D).
+template <int D>
+hipError_t launch_d(const Geometry& g, const void* q, const void* k, const void* v, const int32_t* perm,
+                    const int32_t* idx, const float* w, void* out, float* lse, bool out_fp32, hipStream_t s) {
   const bool dense = idx == nullptr;
   AttendArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -409,7 +414,7 @@ hipError_t launch_attend_bf16(const Geometry& g, const void* q, const void* k, c
   a.perm = perm;
   a.idx = idx;
   a.w = w;
-  a.out = static_cast<uint16_t*>(out);
+  a.out = out;
   a.lse = lse;
   a.H = g.H;
   a.N = g.N;
@@ -421,12 +426,13 @@ hipError_t launch_attend_bf16(const Geometry& g, const void* q, const void* k, c
   a.n_wg = g.B * g.H * g.nQB;
   a.c = g.sm_scale * 1.4426950408889634f;
   const bool p = perm != nullptr;
-  if (g.d == 128) {
-    return g.block_q == 128 ? dispatch_mode<128, 128>(a, g.block_k, dense, p, s)
-                            : dispatch_mode<128, 64>(a, g.block_k, dense, p, s);
+  if (out_fp32) {
+    return g.block_q == 128 ? dispatch_mode<D, 128, true>(a, g.block_k, dense, p, s)
+                            : dispatch_mode<D, 64, true>(a, g.block_k, dense, p, s);
   }
-  return g.block_q == 128 ? dispatch_mode<64, 128>(a, g.block_k, dense, p, s)
-                          : dispatch_mode<64, 64>(a, g.block_k, dense, p, s);
+  return g.block_q == 128 ? dispatch_mode<D, 128, false>(a, g.block_k, dense, p, s)
+                          : dispatch_mode<D, 64, false>(a, g.block_k, dense, p, s);
 }
 
+}  // namespace attend_bf16_impl
 }  // namespace bsa

@@ -22,6 +22,7 @@ bsa_status check_problem(const bsa_problem* p, bsa::Geometry* g) {
   if (p->block_k != 32 && p->block_k != 64 && p->block_k != 128) return BSA_ERR_INVALID_ARG;
   if (p->N_pad % p->block_q != 0 || p->N_pad % p->block_k != 0) return BSA_ERR_INVALID_ARG;
   if (p->dtype != BSA_BF16 && p->dtype != BSA_FP32) return BSA_ERR_INVALID_ARG;
+  if (p->out_fp32 != 0 && p->out_fp32 != 1) return BSA_ERR_INVALID_ARG;
   if (!(p->sm_scale > 0.f) || !isfinite(p->sm_scale)) return BSA_ERR_INVALID_ARG;
   // index arithmetic inside the kernels: rows of one (b, h) and workgroup ids in int32
   if (p->N_pad > (1 << 28)) return BSA_ERR_INVALID_ARG;
@@ -40,6 +41,7 @@ bsa_status check_problem(const bsa_problem* p, bsa::Geometry* g) {
   g->n_valid_units = (p->N + p->block_k - 1) / p->block_k;
   g->L = 0;
   g->bf16 = p->dtype == BSA_BF16;
+  g->out_fp32 = p->out_fp32 == 1;
   g->sm_scale = p->sm_scale;
   g->seed = p->seed;
   return BSA_OK;
@@ -57,6 +59,17 @@ bsa_status check_budget(const bsa_problem* p, bsa::Geometry* g) {
 bsa_status from_hip(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
 
 }  // namespace
+
+namespace bsa {
+
+hipError_t launch_attend_bf16(const Geometry& g, const void* q, const void* k, const void* v,
+                              const int32_t* perm, const int32_t* idx, const float* w, void* out,
+                              float* lse, hipStream_t s) {
+  return g.d == 128 ? launch_attend_bf16_d128(g, q, k, v, perm, idx, w, out, lse, g.out_fp32, s)
+                    : launch_attend_bf16_d64(g, q, k, v, perm, idx, w, out, lse, g.out_fp32, s);
+}
+
+}  // namespace bsa
 
 extern "C" {
 

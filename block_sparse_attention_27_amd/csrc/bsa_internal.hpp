@@ -11,6 +11,7 @@ struct Geometry {
   int B, H, N, N_pad, d, block_q, block_k;
   int nQB, nKU, n_valid_units, L;
   bool bf16;
+  bool out_fp32;  // bf16 inputs with an fp32 output
   float sm_scale;
   uint64_t seed;
 };
@@ -27,6 +28,12 @@ hipError_t launch_select(const Geometry& g, int k_exact, int m_sample, const flo
 
 // ---- attention ----
 // idx/w == nullptr selects the dense variant (every valid key, weight 1).
+hipError_t launch_attend_bf16_d128(const Geometry& g, const void* q, const void* k, const void* v,
+                                   const int32_t* perm, const int32_t* idx, const float* w, void* out,
+                                   float* lse, bool out_fp32, hipStream_t s);
+hipError_t launch_attend_bf16_d64(const Geometry& g, const void* q, const void* k, const void* v,
+                                  const int32_t* perm, const int32_t* idx, const float* w, void* out,
+                                  float* lse, bool out_fp32, hipStream_t s);
 hipError_t launch_attend_bf16(const Geometry& g, const void* q, const void* k, const void* v,
                               const int32_t* perm, const int32_t* idx, const float* w, void* out,
                               float* lse, hipStream_t s);

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 1
+#define BSA_ABI_VERSION 2
 
 typedef enum bsa_status {
   BSA_OK = 0,
@@ -77,10 +77,11 @@ typedef struct bsa_problem {
   int32_t block_k;    /* key-unit rows: 32, 64 or 128 (4, 2 or 1 per 128-key tile) */
   int32_t k_exact;    /* exact-set size k >= 0 */
   int32_t m_sample;   /* sample size m >= 0; 1 <= k+m <= number of valid units */
-  int32_t dtype;      /* bsa_dtype */
+  int32_t dtype;      /* bsa_dtype of Q, K, V */
+  int32_t out_fp32;   /* 0: out has the element type of Q; 1: out is fp32 (always fp32 for BSA_FP32) */
+  int32_t reserved;   /* must be 0 */
   uint64_t seed;      /* sampler seed (Philox4x32-10 key) */
   float sm_scale;     /* logit = sm_scale * <q, k>; finite and > 0 */
-  int32_t reserved;   /* must be 0 */
 } bsa_problem;
 
 /* Returns BSA_ABI_VERSION. */
@@ -144,7 +145,9 @@ bsa_status bsa_select(const bsa_problem* p, const float* S, int32_t* idx, float*
  * The list is used as given (a repeated entry counts twice); entries with an
  * index outside [0, nKU) or a weight that is not > 0 contribute nothing.
  * idx/w may come from bsa_select or from the caller (e.g. a plan reused across
- * denoising steps). lse may be NULL. out has the element type `dtype`.
+ * denoising steps). lse may be NULL. out is fp32 when out_fp32 is 1 or dtype
+ * is BSA_FP32, else bf16; a bf16 out is the fp32 result rounded to nearest
+ * even, bit for bit.
  */
 bsa_status bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* v,
                       const int32_t* perm, const int32_t* idx, const float* w, void* out,

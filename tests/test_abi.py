@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 1
+    assert lib.bsa_abi_version() == 2
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(1) == b"invalid argument"
     assert lib.bsa_status_string(99) == b"unknown status"
@@ -60,20 +60,22 @@ def test_problem_struct_layout_matches_header(tmp_path):
         pytest.skip("no C compiler")
     src = tmp_path / "layout.c"
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "bsa.h"\n'
-                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(bsa_problem),'
+                   'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(bsa_problem),'
                    ' offsetof(bsa_problem, dtype), offsetof(bsa_problem, seed),'
-                   ' offsetof(bsa_problem, sm_scale), offsetof(bsa_problem, reserved)); return 0;}\n')
+                   ' offsetof(bsa_problem, sm_scale), offsetof(bsa_problem, reserved),'
+                   ' offsetof(bsa_problem, out_fp32)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
                     "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
     c_vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     P = bsa.Problem
-    assert c_vals == [ctypes.sizeof(P), P.dtype.offset, P.seed.offset, P.sm_scale.offset, P.reserved.offset]
+    assert c_vals == [ctypes.sizeof(P), P.dtype.offset, P.seed.offset, P.sm_scale.offset, P.reserved.offset,
+                      P.out_fp32.offset]
 
 
 def _good(**kw):
     f = dict(B=1, H=2, N=1000, N_pad=1024, d=128, block_q=128, block_k=64, k_exact=2, m_sample=3,
-             dtype=bsa.BSA_BF16, seed=1, sm_scale=1.0, reserved=0)
+             dtype=bsa.BSA_BF16, out_fp32=0, seed=1, sm_scale=1.0, reserved=0)
     f.update(kw)
     return bsa.Problem(**f)
 
@@ -81,7 +83,7 @@ def _good(**kw):
 BAD = [
     dict(B=0), dict(H=0), dict(N=0), dict(N=2000), dict(d=96), dict(block_q=32), dict(block_k=16),
     dict(N_pad=1000), dict(dtype=7), dict(sm_scale=0.0), dict(sm_scale=float("inf")),
-    dict(sm_scale=float("nan")), dict(reserved=1), dict(N_pad=1 << 29, N=1 << 29),
+    dict(sm_scale=float("nan")), dict(reserved=1), dict(N_pad=1 << 29, N=1 << 29), dict(out_fp32=2),
 ]
 BAD_BUDGET = [dict(k_exact=-1), dict(m_sample=-1), dict(k_exact=0, m_sample=0),
               dict(k_exact=10, m_sample=7)]  # 16 valid units of 64 keys in N = 1000

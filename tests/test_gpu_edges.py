@@ -36,8 +36,16 @@ def _run_and_check(w, tol_out):
     p = bsa.problem_for(w)
     S, qm, km = bsa.score(p, q, k, perm)
     idx, wt = bsa.select(p, S)
-    out, lse = bsa.attend(p, q, k, v, idx, wt, perm, with_lse=True)
-    outd, lsed = bsa.attend_dense(p, q, k, v, perm, with_lse=True)
+    p32 = bsa.Problem.from_buffer_copy(p)
+    p32.out_fp32 = 1
+    out, lse = bsa.attend(p32, q, k, v, idx, wt, perm, with_lse=True)
+    outd, lsed = bsa.attend_dense(p32, q, k, v, perm, with_lse=True)
+    if w.dtype == "bf16":
+        o16 = bsa.attend(p, q, k, v, idx, wt, perm)
+        od16 = bsa.attend_dense(p, q, k, v, perm)
+        torch.cuda.synchronize()
+        assert torch.equal(o16.view(torch.int16), out.to(torch.bfloat16).view(torch.int16))
+        assert torch.equal(od16.view(torch.int16), outd.to(torch.bfloat16).view(torch.int16))
     torch.cuda.synchronize()
     qh, kh, vh = (host_f64(g[x]) for x in ("q", "k", "v"))
     S_ref, qb, kb = oracle.score(qh, kh, w.N, w.block_q, w.block_k, w.sm_scale, g["perm"])
@@ -84,7 +92,9 @@ def test_dense_limit_matches_dense_kernel(dtype):
     w = w.replace(k_exact=4, m_sample=n_valid - 4)
     g, p, (q, k, v, perm), (S, idx, wt, out) = _run_and_check(w, (2e-3, 1e-2) if dtype == "bf16" else (1e-5, 1e-5))
     assert np.all(wt.cpu().numpy() == 1.0)
-    outd = bsa.attend_dense(p, q, k, v, perm)
+    p32 = bsa.Problem.from_buffer_copy(p)
+    p32.out_fp32 = 1
+    outd = bsa.attend_dense(p32, q, k, v, perm)
     torch.cuda.synchronize()
     a, b = to_f64(out), to_f64(outd)
     assert rel_l2(a, b) <= 2e-3 and np.max(np.abs(a - b)) <= 1e-2
@@ -100,7 +110,7 @@ def test_ignored_and_repeated_list_entries():
     w = _small(128, 128, 32, "bf16", False, k=2, m=6)
     g = generate(w)
     q, k, v = (to_device(g[x]) for x in ("q", "k", "v"))
-    p = bsa.problem_for(w)
+    p = bsa.problem_for(w, out_fp32=1)
     rng = np.random.default_rng(5)
     shape = (w.B, w.H, w.n_qblocks, w.list_len)
     idx = rng.integers(0, w.n_valid_units, shape).astype(np.int32)
