@@ -110,6 +110,8 @@ def main(argv=None):
     ap.add_argument("--config", default="wan14b_720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -205,6 +207,14 @@ def main(argv=None):
     elem = 2 if w.dtype == "bf16" else 4
     score_bytes = 2 * w.B * w.H * w.N * w.d * elem + 4 * w.B * w.H * w.n_qblocks * w.n_units
     select_bytes = 4 * w.B * w.H * w.n_qblocks * (w.n_valid_units + 2 * w.list_len)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
