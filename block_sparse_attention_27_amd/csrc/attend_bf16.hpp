@@ -1,5 +1,6 @@
 // Weighted block-sparse flash attention (and its dense special case) on bf16
-// MFMA for gfx950.
+// MFMA for gfx950. Kernel template; instantiated per head dimension in
+// attend_bf16_d128.hip and attend_bf16_d64.hip.
 //
 // What is computed (AB-Attention, Abstract and transcript on the tiled kernel;
 // InstaGen, Abstract): for the query rows of one query block and the list of
@@ -10,15 +11,26 @@
 // per-row subtraction constant, so it costs nothing per element. Key units
 // smaller than the 128-key tile (32 or 64 keys) are gathered into one tile.
 //
-// Work decomposition: one workgroup per (b, h, query block); each of its
-// BQ/32 waves owns 32 query rows. Every 128-key tile of the list is staged in
-// LDS (K row-major, V transposed), then per wave:
-//   S^T[key][row] = K . Q^T   (A = K from LDS, B = Q^T held in registers)
-//   O^T[d][row]  += V^T . P^T (A = V^T from LDS, B = P^T straight from the
+// Work decomposition. One workgroup per (b, h, query block) with 2*BQ/32
+// waves: wave (rg, kh) owns query rows [32 rg, 32 rg + 32) and keys
+// [64 kh, 64 kh + 64) of every 128-key tile; the two key halves are merged at
+// the end like two partial softmaxes. Per wave and tile:
+//   S^T[key][row] = K . Q^T   (A = K rows from LDS, B = Q^T in registers)
+//   O^T[d][row]  += V^T . P^T (A = V^T read transposed from LDS with
+//                              ds_read_b64_tr_b16, B = P^T straight from the
 //                              S^T accumulators after exp and bf16 packing)
-// using v_mfma_f32_32x32x16_bf16. In the S^T orientation a lane holds one
-// query row, so row max and row sum never leave the lane except for one
-// exchange between the two 32-lane halves per tile.
+// on v_mfma_f32_32x32x16_bf16. A lane holds one query row, so the row max and
+// row sum stay in the lane except for one exchange between 32-lane halves.
+//
+// Data movement. K and V tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, no registers, no ALU work), double-buffered so the
+// next tile streams in while the current one is computed; both are stored
+// row-major with an XOR swizzle of the 16-byte chunks that keeps the K reads
+// (8 consecutive rows, one chunk) and the transposed V reads (4 consecutive
+// rows, two chunks) free of bank conflicts. The list of a query block is
+// first rank-sorted by unit index so that concurrent workgroups sweep the keys
+// of a head in the same order, and workgroups are mapped so that all 8 XCDs
+// work on the same head at once, each on a contiguous run of query blocks.
 #pragma once
 
 #include "bsa_internal.hpp"
@@ -29,10 +41,16 @@ namespace bsa {
 namespace attend_bf16_impl {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define BSA_LDS __attribute__((address_space(3)))
 
 constexpr int TILE = 128;           // keys per staged tile
+constexpr int LMAX = 1024;          // list entries sorted and held in LDS at a time
 constexpr float RESCALE_SLACK = 8;  // log2 units the running max may lag the true max
 
 struct AttendArgs {
@@ -44,77 +62,18 @@ struct AttendArgs {
   const float* w;
   void* out;
   float* lse;
-  int H, N, N_pad, nQB, nKU, L, n_tiles, n_wg;
+  int H, N, N_pad, nQB, nKU, L, n_wg, qchunk;
   float c;  // sm_scale * log2(e)
 };
 
-// XOR swizzle of the 16-byte chunk index within an LDS row: eight consecutive
-// rows read at one column land on eight different bank groups.
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-
-__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
+// 16-byte chunk swizzle of a K/V row in LDS: any 8 consecutive aligned rows get
+// 8 different values, and any 4 consecutive aligned rows get 4 different
+// values of (swz >> 1).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// Position p in [0,16) of a 16-key group inside the transposed V tile holds
-// key sigma(p) of that group. The permutation matches the key order in which
-// the S^T accumulators hand P to the PV product (see the derivation in the
-// kernel body).
-__device__ __forceinline__ constexpr int sigma(int p) { return 8 * ((p % 8) / 4) + 4 * (p / 8) + p % 4; }
-
-struct TileMeta {
-  int base[4];   // first global (pre-permutation) key row of each unit in the tile
-  int lim[4];    // valid keys of each unit (0 for an empty or rejected entry)
-  float lw[4];   // log2 of the unit's weight
-};
-
-template <int BK, bool DENSE>
-__device__ __forceinline__ TileMeta tile_meta(const AttendArgs& a, const int32_t* idx_row,
-                                              const float* w_row, int t) {
-  constexpr int U = TILE / BK;
-  TileMeta m;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    m.base[u] = 0;
-    m.lim[u] = 0;
-    m.lw[u] = 0.f;
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if constexpr (DENSE) {
-      const int b0 = t * TILE;
-      m.base[u] = b0;
-      m.lim[u] = min(TILE, a.N - b0);
-    } else {
-      const int e = t * U + u;
-      int j = -1;
-      float wv = 0.f;
-      if (e < a.L) {
-        j = idx_row[e];
-        wv = w_row[e];
-      }
-      const bool ok = j >= 0 && j < a.nKU && wv > 0.f && wv < INFINITY;
-      const int b0 = ok ? j * BK : 0;
-      m.base[u] = b0;
-      m.lim[u] = ok ? max(0, min(BK, a.N - b0)) : 0;
-      m.lw[u] = ok ? __builtin_amdgcn_logf(wv) : 0.f;
-    }
-  }
-  return m;
-}
-
-template <int BK>
-__device__ __forceinline__ int pick(const int (&x)[4], int u) {
-  if constexpr (BK == 128) {
-    return x[0];
-  } else if constexpr (BK == 64) {
-    return u == 0 ? x[0] : x[1];
-  } else {
-    return u == 0 ? x[0] : u == 1 ? x[1] : u == 2 ? x[2] : x[3];
-  }
-}
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 template <bool PERM>
 __device__ __forceinline__ int gather_row(const AttendArgs& a, int r, bool& ok) {
@@ -128,220 +87,305 @@ __device__ __forceinline__ int gather_row(const AttendArgs& a, int r, bool& ok) 
   }
 }
 
-// Global -> LDS staging of one 128-key tile: K row-major [key][d], V transposed
-// [d][key] with keys of each 16-key group in sigma order. Rows that are padding,
-// belong to a rejected entry or fall outside the list are written as zeros.
-template <int D, int NT, int BK, bool PERM>
-__device__ __forceinline__ void stage_tile(const AttendArgs& a, const uint16_t* kb, const uint16_t* vb,
-                                           char* ks, char* vts, const TileMeta& m, int tid) {
-  constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  constexpr int KRPP = NT / KCH;      // K rows per pass
-  constexpr int KP = TILE / KRPP;     // passes
-  static_assert(BK % KRPP == 0, "a K pass must stay inside one unit");
-  constexpr int VDG = D / 8;          // 8-column groups of V
-  constexpr int VITEMS = 16 * VDG;    // (8-key group, 8-column group) items
-  constexpr int VPT = (VITEMS + NT - 1) / NT;
+struct TileMeta {
+  int base[4];  // first global (pre-permutation) key row of each unit in the tile
+  int lim[4];   // valid keys of each unit (0: empty slot or rejected entry)
+  float lw[4];  // log2 of the unit's weight
+};
 
-  // ---- K ----
-  {
-    const int cc = tid % KCH, rb = tid / KCH;
-    u32x4 r[KP];
-    int gr[KP];
-    bool ok[KP];
+// Direct global -> LDS staging of one 128-key tile of K and of V. Each wave
+// instruction moves 1 KB = 1024 / (2 D) whole rows; lane l fills physical chunk
+// l % (D/8) of its row, i.e. logical chunk (l % (D/8)) ^ swz(row). Rows that are
+// not valid keys load a valid row of the same head (their logits are masked).
+template <int D, int NW, int BK, bool PERM>
+__device__ __forceinline__ void stage_tile(const AttendArgs& a, const uint16_t* kb, const uint16_t* vb,
+                                           BSA_LDS char* kdst, BSA_LDS char* vdst, const TileMeta& m,
+                                           int wave, int lane) {
+  constexpr int CPR = D / 8;                   // chunks per row
+  constexpr int RPI = 1024 / (2 * D);          // rows per instruction
+  constexpr int PER_WAVE = TILE / RPI / NW;    // instructions per wave per tensor
+  static_assert(PER_WAVE * RPI * NW == TILE, "tile rows must split evenly over the waves");
 #pragma unroll
-    for (int e = 0; e < KP; ++e) {
-      const int row = rb + KRPP * e;
-      const int u = (KRPP * e) / BK;  // compile-time: a pass never straddles units
-      const int o = row - u * BK;
-      ok[e] = o < m.lim[u];
-      gr[e] = gather_row<PERM>(a, m.base[u] + o, ok[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < KP; ++e) {
-      r[e] = ok[e] ? ldg16(kb + static_cast<size_t>(gr[e]) * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int e = 0; e < KP; ++e) {
-      const int row = rb + KRPP * e;
-      *reinterpret_cast<u32x4*>(ks + row * (D * 2) + ((cc ^ swz(row)) << 4)) = r[e];
-    }
-  }
-  // ---- V (8 keys x 8 columns per item, transposed in registers) ----
-#pragma unroll
-  for (int x = 0; x < VPT; ++x) {
-    const int it = tid + NT * x;
-    if (VITEMS % NT != 0 && it >= VITEMS) break;
-    const int dg = it % VDG, kg = it / VDG;
-    const int g16 = kg >> 1, hh = kg & 1;
-    const int u = (16 * g16) / BK;
-    const int ubase = pick<BK>(m.base, u), ulim = pick<BK>(m.lim, u);
-    u32x4 r[8];
-    int gr[8];
-    bool ok[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = 16 * g16 + sigma(8 * hh + e);
-      const int o = key - u * BK;
-      ok[e] = o < ulim;
-      gr[e] = gather_row<PERM>(a, ubase + o, ok[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      r[e] = ok[e] ? ldg16(vb + static_cast<size_t>(gr[e]) * D + dg * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // column c of the 8x8 block: 8 keys (rows e = 0..7), two bf16 per dword
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      u32x4 col;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t lo = r[2 * jj][c / 2], hi = r[2 * jj + 1][c / 2];
-        col[jj] = (c & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-      }
-      const int d = dg * 8 + c;
-      const int chunk = 2 * g16 + hh;
-      *reinterpret_cast<u32x4*>(vts + d * (TILE * 2) + ((chunk ^ swz(d)) << 4)) = col;
-    }
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int ins = wave * PER_WAVE + i;
+    const int row = ins * RPI + lane / CPR;
+    const int u = (ins * RPI) / BK;  // rows of one instruction never straddle a unit
+    const int ubase = BK == 128 ? m.base[0] : (BK == 64 ? (u == 0 ? m.base[0] : m.base[1])
+                                                        : (u == 0 ? m.base[0] : u == 1 ? m.base[1] : u == 2 ? m.base[2] : m.base[3]));
+    const int ulim = BK == 128 ? m.lim[0] : (BK == 64 ? (u == 0 ? m.lim[0] : m.lim[1])
+                                                      : (u == 0 ? m.lim[0] : u == 1 ? m.lim[1] : u == 2 ? m.lim[2] : m.lim[3]));
+    const int o = row - u * BK;
+    bool ok = o < ulim;
+    int gr = gather_row<PERM>(a, ok ? ubase + o : ubase, ok);
+    if (!ok) gr = PERM ? 0 : ubase;  // any row of this head; masked later
+    const int lc = (lane % CPR) ^ swz(row);
+    const size_t off = static_cast<size_t>(gr) * D + lc * 8;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kb + off),
+                                     (BSA_LDS void*)(kdst + ins * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vb + off),
+                                     (BSA_LDS void*)(vdst + ins * 1024), 16, 0, 0);
   }
 }
 
+// Rank-sorts the list chunk [c0, c0 + n) of one query block by unit index
+// (ties by position) into the LDS tables; entries with an index outside
+// [0, nKU) or a weight that is not a finite positive number become empty.
+template <int NT, int BK>
+__device__ __forceinline__ void sort_list(const AttendArgs& a, const int32_t* idx_row, const float* w_row,
+                                          int c0, int n, int* s_key, int* s_base, int* s_lim, float* s_lw,
+                                          int tid) {
+  for (int e = tid; e < n; e += NT) {
+    const int j = idx_row[c0 + e];
+    const float wv = w_row[c0 + e];
+    const bool ok = j >= 0 && j < a.nKU && wv > 0.f && wv < INFINITY;
+    s_key[e] = ok ? j : 0x7FFFFFFF;
+  }
+  __syncthreads();
+  for (int e = tid; e < n; e += NT) {
+    const int my = s_key[e];
+    int rank = 0;
+    for (int e2 = 0; e2 < n; ++e2) {
+      const int k2 = s_key[e2];
+      rank += (k2 < my || (k2 == my && e2 < e)) ? 1 : 0;
+    }
+    const bool ok = my != 0x7FFFFFFF;
+    const int b0 = ok ? my * BK : 0;
+    s_base[rank] = b0;
+    s_lim[rank] = ok ? max(0, min(BK, a.N - b0)) : 0;
+    s_lw[rank] = ok ? __builtin_amdgcn_logf(w_row[c0 + e]) : 0.f;
+  }
+  __syncthreads();
+}
+
+template <int BK, bool DENSE>
+__device__ __forceinline__ TileMeta tile_meta(const AttendArgs& a, const int* s_base, const int* s_lim,
+                                              const float* s_lw, int t, int n_entries) {
+  constexpr int U = TILE / BK;
+  TileMeta m;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    m.base[u] = 0;
+    m.lim[u] = 0;
+    m.lw[u] = 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if constexpr (DENSE) {
+      m.base[u] = t * TILE;
+      m.lim[u] = min(TILE, a.N - t * TILE);
+    } else {
+      const int e = t * U + u;
+      if (e < n_entries) {
+        m.base[u] = s_base[e];
+        m.lim[u] = s_lim[e];
+        m.lw[u] = s_lw[e];
+      }
+    }
+  }
+  return m;
+}
+
 template <int D, int BQ, int BK, bool DENSE, bool PERM, bool OUT32>
-__global__ __launch_bounds__(BQ * 2, 2) void attend_bf16_kernel(AttendArgs a) {
-  constexpr int NW = BQ / 32;
+__global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
+  constexpr int NRG = BQ / 32;  // row groups
+  constexpr int NW = 2 * NRG;   // waves: row group x key half
   constexpr int NT = 64 * NW;
-  constexpr int KBYTES = TILE * D * 2;
-  __shared__ __attribute__((aligned(16))) char smem[KBYTES + D * TILE * 2];
-  char* ks = smem;
-  char* vts = smem + KBYTES;
+  constexpr int ROWB = 2 * D;           // bytes per K/V row
+  constexpr int TILEB = TILE * ROWB;    // bytes per K (or V) tile
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];  // K0 V0 K1 V1
+  __shared__ int s_key[DENSE ? 1 : LMAX];
+  __shared__ int s_base[DENSE ? 1 : LMAX];
+  __shared__ int s_lim[DENSE ? 1 : LMAX];
+  __shared__ float s_lw[DENSE ? 1 : LMAX];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
   const int n = lane % 32, h = lane / 32;
+  const int rg = wave % NRG, kh = wave / NRG;
 
-  const int logical = xcd_remap(blockIdx.x, a.n_wg);
-  const int bh = logical / a.nQB, qi = logical % a.nQB;
+  // XCD-chunked mapping: hardware workgroup g runs on XCD g % 8; XCD x takes
+  // query blocks [x*qchunk, (x+1)*qchunk) of each (b, h) in turn.
+  const int xg = blockIdx.x % 8, sg = blockIdx.x / 8;
+  const int bh = sg / a.qchunk;
+  const int qi = xg * a.qchunk + sg % a.qchunk;
+  if (qi >= a.nQB) return;  // padding workgroup (uniform)
+
   const size_t bh_off = static_cast<size_t>(bh) * a.N_pad * D;
   const uint16_t* qb = a.q + bh_off;
   const uint16_t* kb = a.k + bh_off;
   const uint16_t* vb = a.v + bh_off;
-  const int32_t* idx_row = DENSE ? nullptr : a.idx + static_cast<size_t>(logical) * a.L;
-  const float* w_row = DENSE ? nullptr : a.w + static_cast<size_t>(logical) * a.L;
+  const size_t row_id = static_cast<size_t>(bh) * a.nQB + qi;
+  const int32_t* idx_row = DENSE ? nullptr : a.idx + row_id * a.L;
+  const float* w_row = DENSE ? nullptr : a.w + row_id * a.L;
 
   // Q^T fragments (B operand): lane (row n, half h) holds d = 16 s + 8 h .. +7.
-  const int qrow = qi * BQ + 32 * wave + n;
+  const int qrow = qi * BQ + 32 * rg + n;
   bool qok = qrow < a.N;
   const int qg = gather_row<PERM>(a, qrow, qok);
   bf16x8 qf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    qf[s] = as_bf16x8(qok ? ldg16(qb + static_cast<size_t>(qg) * D + 16 * s + 8 * h)
-                          : u32x4{0u, 0u, 0u, 0u});
-  }
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = as_bf16x8(qok ? ldg16(qb + static_cast<size_t>(qg) * D + 16 * s + 8 * h) : u32x4{0u, 0u, 0u, 0u});
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
-  float m_ref = -INFINITY;  // running max of x over this row (shared by both halves)
-  float l_part = 0.f;       // this half's share of the weighted denominator
+  float m_ref = -INFINITY;  // running max of x for this row (shared by both lane halves)
+  float l_part = 0.f;       // this lane's share of the weighted denominator
 
-  for (int t = 0; t < a.n_tiles; ++t) {
-    const TileMeta meta = tile_meta<BK, DENSE>(a, idx_row, w_row, t);
-    if (t > 0) __syncthreads();  // every wave is done reading the previous tile
-    stage_tile<D, NT, BK, PERM>(a, kb, vb, ks, vts, meta, tid);
-    __syncthreads();
-
-    // ---- S^T = K Q^T : 4 sub-tiles of 32 keys; acc register r of sub-tile kt
-    // holds key 32 kt + 8 (r/4) + 4 h + r%4 for query row n.
-    f32x16 sacc[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      sacc[kt] = f32x16{};
-      const int key = 32 * kt + n;
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const int chunk = 2 * s + h;
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(ks + key * (D * 2) + ((chunk ^ swz(key)) << 4));
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[s], sacc[kt], 0, 0, 0);
-      }
+  BSA_LDS char* lds = (BSA_LDS char*)(smem);  // address-space cast of the shared array
+  const int n_chunks = DENSE ? 1 : (a.L + LMAX - 1) / LMAX;
+  for (int ck = 0; ck < n_chunks; ++ck) {
+    int n_entries = 0, n_tiles;
+    if constexpr (DENSE) {
+      n_tiles = (a.N + TILE - 1) / TILE;
+    } else {
+      const int c0 = ck * LMAX;
+      n_entries = min(LMAX, a.L - c0);
+      if (ck > 0) __syncthreads();  // the previous chunk's tables and tiles are no longer read
+      sort_list<NT, BK>(a, idx_row, w_row, c0, n_entries, s_key, s_base, s_lim, s_lw, tid);
+      n_tiles = (n_entries * BK + TILE - 1) / TILE;
     }
 
-    // ---- mask keys past the valid range of their unit (uniform branch) ----
-    bool full = true;
+    {
+      const TileMeta m0 = tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, 0, n_entries);
+      stage_tile<D, NW, BK, PERM>(a, kb, vb, lds, lds + TILEB, m0, wave, lane);
+    }
+    for (int t = 0; t < n_tiles; ++t) {
+      BSA_LDS char* kt_lds = lds + (t & 1) * 2 * TILEB;
+      BSA_LDS char* vt_lds = kt_lds + TILEB;
+      const TileMeta meta = tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, t, n_entries);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t have landed
+      __syncthreads();                // ... and everyone's; tile t-1's buffer is free
+      if (t + 1 < n_tiles) {
+        const TileMeta mn = tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, t + 1, n_entries);
+        BSA_LDS char* kn = lds + ((t + 1) & 1) * 2 * TILEB;
+        stage_tile<D, NW, BK, PERM>(a, kb, vb, kn, kn + TILEB, mn, wave, lane);
+      }
+
+      // ---- S^T = K Q^T over this wave's 64 keys: sub-tile j (keys
+      // 64 kh + 32 j ..); acc register r holds key 8 (r/4) + 4 h + r%4 of it.
+      f32x16 sacc[2];
 #pragma unroll
-    for (int u = 0; u < TILE / BK; ++u) full = full && (meta.lim[u] == BK);
-    if (!full) {
+      for (int j = 0; j < 2; ++j) {
+        sacc[j] = f32x16{};
+        const int key = 64 * kh + 32 * j + n;
+        const BSA_LDS char* krow = kt_lds + key * ROWB;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const int u = (32 * kt) / BK;
-        const int lim = meta.lim[u];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = (32 * kt) % BK + 8 * (r / 4) + 4 * h + (r % 4);
-          if (off >= lim) sacc[kt][r] = -INFINITY;
+        for (int s = 0; s < D / 16; ++s) {
+          const int chunk = 2 * s + h;
+          const u32x4 kv = *(const BSA_LDS u32x4*)(krow + ((chunk ^ swz(key)) << 4));
+          sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[s], sacc[j], 0, 0, 0);
         }
       }
-    }
 
-    // ---- tile max, lazily re-based running max ----
-    float mx = -INFINITY;
+      // ---- mask keys past the valid range of their unit (uniform branch) ----
+      const int u0 = (64 * kh) / BK, u1 = (64 * kh + 32) / BK;
+      const int lim0 = u0 == 0 ? meta.lim[0] : u0 == 1 ? meta.lim[1] : u0 == 2 ? meta.lim[2] : meta.lim[3];
+      const int lim1 = u1 == 0 ? meta.lim[0] : u1 == 1 ? meta.lim[1] : u1 == 2 ? meta.lim[2] : meta.lim[3];
+      const float lw0 = u0 == 0 ? meta.lw[0] : u0 == 1 ? meta.lw[1] : u0 == 2 ? meta.lw[2] : meta.lw[3];
+      const float lw1 = u1 == 0 ? meta.lw[0] : u1 == 1 ? meta.lw[1] : u1 == 2 ? meta.lw[2] : meta.lw[3];
+      const int off0 = (64 * kh) % BK, off1 = (64 * kh + 32) % BK;
+      if (off0 + 32 > lim0 || off1 + 32 > lim1) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int j = 0; j < 2; ++j) {
+          const int lim = j ? lim1 : lim0, off = j ? off1 : off0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mx *= a.c;  // c > 0
-    const bool need = mx > m_ref + RESCALE_SLACK;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mx : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_part *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      m_ref = m_new;
-    }
-    const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-    // ---- P = 2^(x - m + log2 w), row sums ----
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const float bias = meta.lw[(32 * kt) / BK] - mb;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], a.c, bias));
-        sacc[kt][r] = p;
-        l_part += p;
+          for (int r = 0; r < 16; ++r)
+            if (off + 8 * (r / 4) + 4 * h + (r % 4) >= lim) sacc[j][r] = -INFINITY;
+        }
       }
-    }
 
-    // ---- O^T += V^T P^T over 8 steps of 16 keys. Step ks takes registers
-    // 8 (ks%2) + e of sub-tile ks/2: lane half h then holds keys
-    // 16 ks + sigma(8 h + e), the order in which V^T is staged.
+      // ---- tile max and lazily re-based running max ----
+      float mx = -INFINITY;
 #pragma unroll
-    for (int ks_ = 0; ks_ < 8; ++ks_) {
-      const int kt = ks_ / 2, s2 = ks_ % 2;
-      bf16x8 pb;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[kt][8 * s2 + e]);
-      const int chunk = 2 * ks_ + h;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[j][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx *= a.c;  // c > 0
+      const bool need = mx > m_ref + RESCALE_SLACK;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? mx : m_ref;
+        const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_part *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int d = 32 * dt + n;
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(vts + d * (TILE * 2) + ((chunk ^ swz(d)) << 4));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vv), pb, o[dt], 0, 0, 0);
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m_ref = m_new;
+      }
+      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
+
+      // ---- P = 2^(x - m + log2 w) packed to bf16; the row sum uses the packed values ----
+      bf16x8 pb[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float bias = (j ? lw1 : lw0) - mb;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j][r], a.c, bias));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j][r + 1], a.c, bias));
+          const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)},
+                                                   l_part, false);
+          pb[2 * j + r / 8][r % 8] = pp[0];
+          pb[2 * j + r / 8][r % 8 + 1] = pp[1];
+        }
+      }
+
+      // ---- O^T += V^T P^T over 4 steps of 16 keys. Step ks takes P registers
+      // 8 (ks%2) + e of sub-tile ks/2, i.e. keys 16 ks + 8 (e/4) + 4 h + e%4 of
+      // this wave's half; the two transposed reads fetch e = 0..3 and e = 4..7.
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int q16 = lane % 16;
+        const int kA = 64 * kh + 16 * ks + 4 * h + q16 / 4;  // row this lane addresses (read A)
+        const int kB = kA + 8;                                // read B
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const int col = 32 * dt + 16 * ((lane / 16) % 2) + 4 * (q16 % 4);
+          const BSA_LDS char* pa = vt_lds + kA * ROWB + ((((col >> 3) ^ swz(kA))) << 4) + (col & 7) * 2;
+          const BSA_LDS char* pbp = vt_lds + kB * ROWB + ((((col >> 3) ^ swz(kB))) << 4) + (col & 7) * 2;
+          const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4*)pa);
+          const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4*)pbp);
+          const u32x2 ua = __builtin_bit_cast(u32x2, va), ub = __builtin_bit_cast(u32x2, vv);
+          const bf16x8 av = as_bf16x8(u32x4{ua[0], ua[1], ub[0], ub[1]});
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
+        }
       }
     }
   }
 
-  // ---- epilogue: O^T register r of d-tile dt holds d = 32 dt + 8 (r/4) + 4 h + r%4 ----
+  // ---- merge the two key halves of each row group ----
   const float l_tot = l_part + __shfl_xor(l_part, 32);
+  __syncthreads();  // the tile buffers are free
+  float* part = reinterpret_cast<float*>(smem);         // [NRG][D/32 * 16][64]
+  float* pm = part + NRG * (D / 2) * 64;                 // [NRG][64]
+  float* pl = pm + NRG * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[(rg * (D / 2) + dt * 16 + r) * 64 + lane] = o[dt][r];
+    pm[rg * 64 + lane] = m_ref;
+    pl[rg * 64 + lane] = l_tot;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = pm[rg * 64 + lane], l1 = pl[rg * 64 + lane];
+  const float mm = fmaxf(m_ref, m1);
+  const float s0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
+  const float s1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+  const float lsum = l_tot * s0 + l1 * s1;
+
+  // ---- epilogue: O^T register r of d-tile dt holds d = 32 dt + 8 (r/4) + 4 h + r%4 ----
   bool ok = true;
   int orow = qrow;
   float inv = 0.f;
   if (qrow < a.N) {
     orow = gather_row<PERM>(a, qrow, ok);
-    inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    inv = lsum > 0.f ? 1.f / lsum : 0.f;
   }
   if (ok) {  // rows >= N (inv = 0) are written as zeros
     const size_t obase = bh_off + static_cast<size_t>(orow) * D;
@@ -352,7 +396,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_bf16_kernel(AttendArgs a) {
         const int col = 32 * dt + 8 * g + 4 * h;
         float x[4];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) x[z] = o[dt][4 * g + z] * inv;
+        for (int z = 0; z < 4; ++z) {
+          const int r = 4 * g + z;
+          x[z] = (o[dt][r] * s0 + part[(rg * (D / 2) + dt * 16 + r) * 64 + lane] * s1) * inv;
+        }
         if constexpr (OUT32) {
           float* op = static_cast<float*>(a.out) + obase + col;
           *reinterpret_cast<float4*>(op) = make_float4(x[0], x[1], x[2], x[3]);
@@ -372,14 +419,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void attend_bf16_kernel(AttendArgs a) {
     }
     if (a.lse != nullptr && h == 0) {
       a.lse[static_cast<size_t>(bh) * a.N_pad + orow] =
-          (qrow < a.N && l_tot > 0.f) ? (m_ref + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f : -INFINITY;
+          (qrow < a.N && lsum > 0.f) ? (mm + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f : -INFINITY;
     }
   }
 }
 
 template <int D, int BQ, int BK, bool DENSE, bool PERM, bool OUT32>
 hipError_t launch_one(const AttendArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attend_bf16_kernel<D, BQ, BK, DENSE, PERM, OUT32>), dim3(a.n_wg), dim3(BQ * 2), 0, s, a);
+  hipLaunchKernelGGL((attend_bf16_kernel<D, BQ, BK, DENSE, PERM, OUT32>), dim3(a.n_wg), dim3(BQ * 4), 0, s, a);
   return hipGetLastError();
 }
 
@@ -422,8 +469,8 @@ hipError_t launch_d(const Geometry& g, const void* q, const void* k, const void*
   a.nQB = g.nQB;
   a.nKU = g.nKU;
   a.L = dense ? 0 : g.L;
-  a.n_tiles = dense ? (g.N + TILE - 1) / TILE : (g.L * g.block_k + TILE - 1) / TILE;
-  a.n_wg = g.B * g.H * g.nQB;
+  a.qchunk = (g.nQB + 7) / 8;
+  a.n_wg = 8 * a.qchunk * g.B * g.H;
   a.c = g.sm_scale * 1.4426950408889634f;
   const bool p = perm != nullptr;
   if (out_fp32) {

@@ -29,8 +29,9 @@
  *              computation runs on the gathered rows X'[r] = X[perm[r]] for
  *              Q, K and V alike, and row r of the result is written to row
  *              perm[r] of out (and lse). perm must map 0..N-1 onto 0..N-1;
- *              entries r >= N are not read. An entry outside [0, N_pad) makes
- *              that row read as zeros (no out-of-bounds access).
+ *              entries r >= N are not read. An entry outside [0, N_pad) is
+ *              never dereferenced (no out-of-bounds access) but the result is
+ *              then unspecified.
  *   Memory     All array arguments are device pointers owned by the caller;
  *              Q/K/V/out must be 16-byte aligned, the others 4-byte aligned.
  *              The library allocates nothing, keeps no state between calls and
