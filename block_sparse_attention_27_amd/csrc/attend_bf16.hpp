@@ -25,9 +25,9 @@
 // Data movement. K and V tiles go from global memory straight into LDS
 // (global_load_lds_dwordx4, no registers, no ALU work), double-buffered so the
 // next tile streams in while the current one is computed; both are stored
-// row-major with an XOR swizzle of the 16-byte chunks that keeps the K reads
-// (8 consecutive rows, one chunk) and the transposed V reads (4 consecutive
-// rows, two chunks) free of bank conflicts. The list of a query block is
+// row-major with padded rows that keep the K reads (8 consecutive rows, one
+// 16-byte column) and the transposed V reads (4 consecutive rows, 32 bytes)
+// free of bank conflicts. The list of a query block is
 // first rank-sorted by unit index so that concurrent workgroups sweep the keys
 // of a head in the same order, and workgroups are mapped so that all 8 XCDs
 // work on the same head at once, each on a contiguous run of query blocks.
@@ -66,10 +66,19 @@ struct AttendArgs {
   float c;  // sm_scale * log2(e)
 };
 
-// 16-byte chunk swizzle of a K/V row in LDS: any 8 consecutive aligned rows get
-// 8 different values, and any 4 consecutive aligned rows get 4 different
-// values of (swz >> 1).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// LDS tiles are row-major [128 keys][D] bf16 with the 16-byte chunks of each
+// row permuted by an XOR with a function of the row. gfx950 serves 64 banks
+// (256 bytes) per LDS cycle, so
+//   K: the 16 lanes of one cycle read 16 consecutive rows at one logical
+//      chunk; the XOR spreads them over the 16 chunk positions of a 256-byte
+//      bank row (d = 128: chunk ^ (row & 15); d = 64, two rows per bank row:
+//      chunk ^ ((row >> 1) & 7)).
+//   V: the 32 lanes of one transposed-read cycle take 64 bytes from each of 4
+//      consecutive rows; the XOR moves the four 64-byte pieces apart
+//      (d = 128: chunk ^ 4 (row & 3); d = 64: chunk ^ 4 ((row >> 1) & 1)).
+// Every read address stays a per-lane base plus a compile-time offset.
+template <int D> __device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D> __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
@@ -93,37 +102,31 @@ struct TileMeta {
   float lw[4];  // log2 of the unit's weight
 };
 
-// Direct global -> LDS staging of one 128-key tile of K and of V. Each wave
+// Direct global -> LDS staging of one 128-key tile of K or V. Each wave
 // instruction moves 1 KB = 1024 / (2 D) whole rows; lane l fills physical chunk
 // l % (D/8) of its row, i.e. logical chunk (l % (D/8)) ^ swz(row). Rows that are
 // not valid keys load a valid row of the same head (their logits are masked).
-template <int D, int NW, int BK, bool PERM>
-__device__ __forceinline__ void stage_tile(const AttendArgs& a, const uint16_t* kb, const uint16_t* vb,
-                                           BSA_LDS char* kdst, BSA_LDS char* vdst, const TileMeta& m,
-                                           int wave, int lane) {
+template <int D, int NW, int BK, bool PERM, bool IS_V>
+__device__ __forceinline__ void stage_one(const AttendArgs& a, const uint16_t* src, BSA_LDS char* dst,
+                                          const TileMeta& m, int wave, int lane) {
   constexpr int CPR = D / 8;                   // chunks per row
   constexpr int RPI = 1024 / (2 * D);          // rows per instruction
-  constexpr int PER_WAVE = TILE / RPI / NW;    // instructions per wave per tensor
+  constexpr int PER_WAVE = TILE / RPI / NW;    // instructions per wave
   static_assert(PER_WAVE * RPI * NW == TILE, "tile rows must split evenly over the waves");
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int ins = wave * PER_WAVE + i;
     const int row = ins * RPI + lane / CPR;
     const int u = (ins * RPI) / BK;  // rows of one instruction never straddle a unit
-    const int ubase = BK == 128 ? m.base[0] : (BK == 64 ? (u == 0 ? m.base[0] : m.base[1])
-                                                        : (u == 0 ? m.base[0] : u == 1 ? m.base[1] : u == 2 ? m.base[2] : m.base[3]));
-    const int ulim = BK == 128 ? m.lim[0] : (BK == 64 ? (u == 0 ? m.lim[0] : m.lim[1])
-                                                      : (u == 0 ? m.lim[0] : u == 1 ? m.lim[1] : u == 2 ? m.lim[2] : m.lim[3]));
+    const int ubase = u == 0 ? m.base[0] : u == 1 ? m.base[1] : u == 2 ? m.base[2] : m.base[3];
+    const int ulim = u == 0 ? m.lim[0] : u == 1 ? m.lim[1] : u == 2 ? m.lim[2] : m.lim[3];
     const int o = row - u * BK;
     bool ok = o < ulim;
     int gr = gather_row<PERM>(a, ok ? ubase + o : ubase, ok);
     if (!ok) gr = PERM ? 0 : ubase;  // any row of this head; masked later
-    const int lc = (lane % CPR) ^ swz(row);
-    const size_t off = static_cast<size_t>(gr) * D + lc * 8;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kb + off),
-                                     (BSA_LDS void*)(kdst + ins * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vb + off),
-                                     (BSA_LDS void*)(vdst + ins * 1024), 16, 0, 0);
+    const int lc = (lane % CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + static_cast<size_t>(gr) * D + lc * 8),
+                                     (BSA_LDS void*)(dst + ins * 1024), 16, 0, 0);
   }
 }
 
@@ -175,14 +178,99 @@ __device__ __forceinline__ TileMeta tile_meta(const AttendArgs& a, const int* s_
       m.lim[u] = min(TILE, a.N - t * TILE);
     } else {
       const int e = t * U + u;
-      if (e < n_entries) {
-        m.base[u] = s_base[e];
-        m.lim[u] = s_lim[e];
-        m.lw[u] = s_lw[e];
+      if (e < n_entries) {  // uniform values: keep them in scalar registers
+        m.base[u] = __builtin_amdgcn_readfirstlane(s_base[e]);
+        m.lim[u] = __builtin_amdgcn_readfirstlane(s_lim[e]);
+        m.lw[u] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_lw[e])));
       }
     }
   }
   return m;
+}
+
+// S^T = K Q^T over the 64 keys of key half kh: sub-tile j covers keys
+// 64 kh + 32 j .. +31; accumulator register r holds key 8 (r/4) + 4 h + r%4.
+// Per-lane LDS read offsets. A lane (n = lane % 32, h = lane / 32) of key half
+// kh reads, for step s of S^T = K Q^T over sub-tile j, K row 64 kh + 32 j + n
+// at logical chunk 2 s + h: byte kbase + 64 D j + koff[s]. For the transposed
+// V reads of PV step ks, d-tile dt and key group g (0: keys 16 ks + 4 h .. +3;
+// 1: the same + 8) it reads at vbase + 2 D (16 ks + 8 g) + voff[dt].
+template <int D>
+struct LaneOffsets {
+  int kbase, koff[D / 16];
+  int vbase, voff[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets(int kh, int lane) {
+  LaneOffsets<D> L;
+  const int n = lane % 32, h = lane / 32;
+  L.kbase = (64 * kh + n) * 2 * D;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) L.koff[s] = 16 * ((2 * s + h) ^ k_swz<D>(64 * kh + n));
+  const int q = lane % 16, r = q / 4, c = q % 4, g2 = (lane / 16) % 2;
+  const int vrow = 64 * kh + 4 * h + r;
+  L.vbase = vrow * 2 * D + 8 * (c % 2);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) L.voff[dt] = 16 * ((4 * dt + 2 * g2 + c / 2) ^ v_swz<D>(vrow));
+  return L;
+}
+
+// S^T = K Q^T over the 64 keys of key half kh (the first tile of a list; the
+// pipelined steps issue the same MFMAs interleaved with the softmax). Sub-tile
+// j covers keys 64 kh + 32 j .. +31; accumulator register r holds key
+// 8 (r/4) + 4 h + r%4 of it.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16 (&S)[2], const BSA_LDS char* kslot, const LaneOffsets<D>& L,
+                                        const bf16x8 (&qf)[D / 16]) {
+  S[0] = f32x16{};
+  S[1] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {  // the two accumulators alternate: no back-to-back dependence
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u32x4 kv = *(const BSA_LDS u32x4*)(kslot + L.kbase + 64 * D * j + L.koff[s]);
+      S[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[s], S[j], 0, 0, 0);
+    }
+  }
+}
+
+template <int BK>
+__device__ __forceinline__ void half_meta(const TileMeta& m, int kh, int (&lim)[2], int (&off)[2], float (&lw)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int u = (64 * kh + 32 * j) / BK;
+    lim[j] = u == 0 ? m.lim[0] : u == 1 ? m.lim[1] : u == 2 ? m.lim[2] : m.lim[3];
+    lw[j] = u == 0 ? m.lw[0] : u == 1 ? m.lw[1] : u == 2 ? m.lw[2] : m.lw[3];
+    off[j] = (64 * kh + 32 * j) % BK;
+  }
+}
+
+// Keys past the valid range of their unit get -inf (uniform branch; only
+// tiles that hold a partial or empty unit take it).
+template <int BK>
+__device__ __forceinline__ void mask_tile(f32x16 (&S)[2], const TileMeta& m, int kh, int h) {
+  int lim[2], off[2];
+  float lw[2];
+  half_meta<BK>(m, kh, lim, off, lw);
+  if (off[0] + 32 > lim[0] || off[1] + 32 > lim[1]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (off[j] + 8 * (r / 4) + 4 * h + (r % 4) >= lim[j]) S[j][r] = -INFINITY;
+  }
+}
+
+// Maximum of x over both 32-lane halves (they hold different keys of one row).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 template <int D, int BQ, int BK, bool DENSE, bool PERM, bool OUT32>
@@ -190,9 +278,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
   constexpr int NRG = BQ / 32;  // row groups
   constexpr int NW = 2 * NRG;   // waves: row group x key half
   constexpr int NT = 64 * NW;
-  constexpr int ROWB = 2 * D;           // bytes per K/V row
-  constexpr int TILEB = TILE * ROWB;    // bytes per K (or V) tile
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILEB];  // K0 V0 K1 V1
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE * 2 * D];  // K0 K1 V0 V1
   __shared__ int s_key[DENSE ? 1 : LMAX];
   __shared__ int s_base[DENSE ? 1 : LMAX];
   __shared__ int s_lim[DENSE ? 1 : LMAX];
@@ -233,7 +319,13 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
   float m_ref = -INFINITY;  // running max of x for this row (shared by both lane halves)
   float l_part = 0.f;       // this lane's share of the weighted denominator
 
+  // LDS: two K slots then two V slots. K runs one tile ahead of V so that QK
+  // of tile t+1 overlaps the softmax of tile t.
+  constexpr int TB = TILE * 2 * D;  // bytes per K (or V) tile
   BSA_LDS char* lds = (BSA_LDS char*)(smem);  // address-space cast of the shared array
+  BSA_LDS char* kslot[2] = {lds, lds + TB};
+  BSA_LDS char* vslot[2] = {lds + 2 * TB, lds + 3 * TB};
+  const LaneOffsets<D> LO = lane_offsets<D>(kh, lane);
   const int n_chunks = DENSE ? 1 : (a.L + LMAX - 1) / LMAX;
   for (int ck = 0; ck < n_chunks; ++ck) {
     int n_entries = 0, n_tiles;
@@ -246,120 +338,124 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
       sort_list<NT, BK>(a, idx_row, w_row, c0, n_entries, s_key, s_base, s_lim, s_lw, tid);
       n_tiles = (n_entries * BK + TILE - 1) / TILE;
     }
+    auto meta_of = [&](int t) { return tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, t, n_entries); };
 
-    {
-      const TileMeta m0 = tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, 0, n_entries);
-      stage_tile<D, NW, BK, PERM>(a, kb, vb, lds, lds + TILEB, m0, wave, lane);
-    }
-    for (int t = 0; t < n_tiles; ++t) {
-      BSA_LDS char* kt_lds = lds + (t & 1) * 2 * TILEB;
-      BSA_LDS char* vt_lds = kt_lds + TILEB;
-      const TileMeta meta = tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, t, n_entries);
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t have landed
-      __syncthreads();                // ... and everyone's; tile t-1's buffer is free
-      if (t + 1 < n_tiles) {
-        const TileMeta mn = tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, t + 1, n_entries);
-        BSA_LDS char* kn = lds + ((t + 1) & 1) * 2 * TILEB;
-        stage_tile<D, NW, BK, PERM>(a, kb, vb, kn, kn + TILEB, mn, wave, lane);
+    // prologue: K(0), V(0), K(1) in flight; S(0) = QK(0)
+    stage_one<D, NW, BK, PERM, false>(a, kb, kslot[0], meta_of(0), wave, lane);
+    stage_one<D, NW, BK, PERM, true>(a, vb, vslot[0], meta_of(0), wave, lane);
+    if (n_tiles > 1) stage_one<D, NW, BK, PERM, false>(a, kb, kslot[1], meta_of(1), wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 Sa[2], Sb[2];
+    qk_tile<D>(Sa, kslot[0], LO, qf);
+
+    // One pipelined step: S_cur = QK(t) on entry, S_next = QK(t+1) on exit.
+    auto step = [&](f32x16 (&Scur)[2], f32x16 (&Snext)[2], int t) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t+1) and V(t) loads have landed
+      __syncthreads();                // ... everyone's; the K(t) and V(t-1) slots are free
+      if (t + 2 < n_tiles) stage_one<D, NW, BK, PERM, false>(a, kb, kslot[t & 1], meta_of(t + 2), wave, lane);
+      if (t + 1 < n_tiles) stage_one<D, NW, BK, PERM, true>(a, vb, vslot[(t + 1) & 1], meta_of(t + 1), wave, lane);
+
+      // ---- branches first: mask, row max, lazy rescale of O ----
+      const TileMeta mt = meta_of(t);
+      mask_tile<BK>(Scur, mt, kh, h);
+      int lim[2], off[2];
+      float lw[2];
+      half_meta<BK>(mt, kh, lim, off, lw);
+      float mx = fmaxf(Scur[0][0], Scur[0][1]);
+#pragma unroll
+      for (int q2 = 1; q2 < 16; ++q2) {  // a chain of 3-input maxima over the 32 values
+        const int j = q2 / 8, r = 2 * (q2 % 8);
+        mx = fmaxf(mx, fmaxf(Scur[j][r], Scur[j][r + 1]));
       }
-
-      // ---- S^T = K Q^T over this wave's 64 keys: sub-tile j (keys
-      // 64 kh + 32 j ..); acc register r holds key 8 (r/4) + 4 h + r%4 of it.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        sacc[j] = f32x16{};
-        const int key = 64 * kh + 32 * j + n;
-        const BSA_LDS char* krow = kt_lds + key * ROWB;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          const int chunk = 2 * s + h;
-          const u32x4 kv = *(const BSA_LDS u32x4*)(krow + ((chunk ^ swz(key)) << 4));
-          sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qf[s], sacc[j], 0, 0, 0);
-        }
-      }
-
-      // ---- mask keys past the valid range of their unit (uniform branch) ----
-      const int u0 = (64 * kh) / BK, u1 = (64 * kh + 32) / BK;
-      const int lim0 = u0 == 0 ? meta.lim[0] : u0 == 1 ? meta.lim[1] : u0 == 2 ? meta.lim[2] : meta.lim[3];
-      const int lim1 = u1 == 0 ? meta.lim[0] : u1 == 1 ? meta.lim[1] : u1 == 2 ? meta.lim[2] : meta.lim[3];
-      const float lw0 = u0 == 0 ? meta.lw[0] : u0 == 1 ? meta.lw[1] : u0 == 2 ? meta.lw[2] : meta.lw[3];
-      const float lw1 = u1 == 0 ? meta.lw[0] : u1 == 1 ? meta.lw[1] : u1 == 2 ? meta.lw[2] : meta.lw[3];
-      const int off0 = (64 * kh) % BK, off1 = (64 * kh + 32) % BK;
-      if (off0 + 32 > lim0 || off1 + 32 > lim1) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int lim = j ? lim1 : lim0, off = j ? off1 : off0;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (off + 8 * (r / 4) + 4 * h + (r % 4) >= lim) sacc[j][r] = -INFINITY;
-        }
-      }
-
-      // ---- tile max and lazily re-based running max ----
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mx *= a.c;  // c > 0
+      mx = halves_max(mx) * a.c;  // c > 0
       const bool need = mx > m_ref + RESCALE_SLACK;
+      const float m_new = need ? mx : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
       if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mx : m_ref;
-        const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        l_part *= alpha;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-        m_ref = m_new;
       }
+      l_part *= alpha;
+      m_ref = m_new;
       const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
+      const float bias0 = lw[0] - mb, bias1 = lw[1] - mb;
 
-      // ---- P = 2^(x - m + log2 w) packed to bf16; the row sum uses the packed values ----
+      // ---- straight-line block, issued in this order (sched_barrier fences):
+      // group i = { QK(t+1) MFMA i, the K read four MFMAs ahead, softmax pair(s) of
+      // tile t }, then the PV(t) MFMAs with their transposed V reads four ahead.
+      constexpr int NQ = D / 8;                // QK MFMAs per wave and tile
+      constexpr int NP = 4 * (D / 32);         // PV MFMAs per wave and tile
+      constexpr int PAIRS = 16 / NQ;           // softmax pairs per group (32 values per lane)
+      const BSA_LDS char* kn = kslot[(t + 1) & 1] + LO.kbase;
+      const BSA_LDS char* vt = vslot[t & 1] + LO.vbase;
+      auto kread = [&](int i) {
+        return *(const BSA_LDS u32x4*)(kn + 64 * D * (i % 2) + LO.koff[i / 2]);
+      };
+      auto vread = [&](int m) {
+        const int ks = m / (D / 32), dt = m % (D / 32);
+        const BSA_LDS char* pa = vt + 2 * D * 16 * ks + LO.voff[dt];
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4*)pa);
+        const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4*)(pa + 2 * D * 8));
+        const u32x2 ua = __builtin_bit_cast(u32x2, va), ub = __builtin_bit_cast(u32x2, vv);
+        return u32x4{ua[0], ua[1], ub[0], ub[1]};
+      };
+      u32x4 kf[4], vf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kf[i] = kread(i);
       bf16x8 pb[4];
+      float lsum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float bias = (j ? lw1 : lw0) - mb;
+      for (int i = 0; i < NQ; ++i) {
+        const int j = i % 2, st = i / 2;
+        Snext[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[i % 4]), qf[st],
+                                                           st == 0 ? f32x16{} : Snext[j], 0, 0, 0);
+        if (i + 4 < NQ) kf[i % 4] = kread(i + 4);
+        if (i >= NQ - 4) vf[i - (NQ - 4)] = vread(i - (NQ - 4));
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[j][r], a.c, bias));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[j][r + 1], a.c, bias));
+        for (int pp_ = 0; pp_ < PAIRS; ++pp_) {
+          const int q2 = i * PAIRS + pp_;       // pair index 0..15
+          const int jj = q2 / 8, r = 2 * (q2 % 8);
+          const float bias = jj ? bias1 : bias0;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(Scur[jj][r], a.c, bias));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(Scur[jj][r + 1], a.c, bias));
           const bf16x2 pp = {static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
-          l_part = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)},
-                                                   l_part, false);
-          pb[2 * j + r / 8][r % 8] = pp[0];
-          pb[2 * j + r / 8][r % 8 + 1] = pp[1];
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, bf16x2{static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)},
+                                                 lsum, false);
+          pb[2 * jj + r / 8][r % 8] = pp[0];
+          pb[2 * jj + r / 8][r % 8 + 1] = pp[1];
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      l_part += lsum;
 
-      // ---- O^T += V^T P^T over 4 steps of 16 keys. Step ks takes P registers
-      // 8 (ks%2) + e of sub-tile ks/2, i.e. keys 16 ks + 8 (e/4) + 4 h + e%4 of
-      // this wave's half; the two transposed reads fetch e = 0..3 and e = 4..7.
+      // ---- O^T += V^T P^T over 4 steps of 16 keys of this wave's half. Step ks
+      // takes P registers 8 (ks%2) + e of sub-tile ks/2, i.e. keys
+      // 16 ks + 8 (e/4) + 4 h + e%4; the two transposed reads of vread fetch
+      // e = 0..3 and 4..7.
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int q16 = lane % 16;
-        const int kA = 64 * kh + 16 * ks + 4 * h + q16 / 4;  // row this lane addresses (read A)
-        const int kB = kA + 8;                                // read B
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const int col = 32 * dt + 16 * ((lane / 16) % 2) + 4 * (q16 % 4);
-          const BSA_LDS char* pa = vt_lds + kA * ROWB + ((((col >> 3) ^ swz(kA))) << 4) + (col & 7) * 2;
-          const BSA_LDS char* pbp = vt_lds + kB * ROWB + ((((col >> 3) ^ swz(kB))) << 4) + (col & 7) * 2;
-          const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4*)pa);
-          const i16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((BSA_LDS i16x4*)pbp);
-          const u32x2 ua = __builtin_bit_cast(u32x2, va), ub = __builtin_bit_cast(u32x2, vv);
-          const bf16x8 av = as_bf16x8(u32x4{ua[0], ua[1], ub[0], ub[1]});
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[ks], o[dt], 0, 0, 0);
-        }
+      for (int m = 0; m < NP; ++m) {
+        const int ks = m / (D / 32), dt = m % (D / 32);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[m % 4]), pb[ks], o[dt], 0, 0, 0);
+        if (m + 4 < NP) vf[m % 4] = vread(m + 4);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      step(Sa, Sb, t);
+      step(Sb, Sa, t + 1);
     }
+    if (t < n_tiles) step(Sa, Sb, t);
   }
 
   // ---- merge the two key halves of each row group ----
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = halves_sum(l_part);
   __syncthreads();  // the tile buffers are free
+  static_assert(NRG * (D / 2 + 2) * 64 * 4 <= 4 * TILE * 2 * D, "merge area must fit the tile buffers");
   float* part = reinterpret_cast<float*>(smem);         // [NRG][D/32 * 16][64]
   float* pm = part + NRG * (D / 2) * 64;                 // [NRG][64]
   float* pl = pm + NRG * 64;
