@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-ATTEND_SOURCE = os.path.join(ROOT, "block_sparse_attention_27_amd", "csrc", "attend_bf16.hip")
+ATTEND_SOURCE = os.path.join(ROOT, "block_sparse_attention_27_amd", "csrc", "attend_bf16.hpp")
 
 
 def _log(msg):

@@ -37,6 +37,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace bsa {
 namespace attend_bf16_impl {
 
@@ -278,7 +280,14 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
   constexpr int NRG = BQ / 32;  // row groups
   constexpr int NW = 2 * NRG;   // waves: row group x key half
   constexpr int NT = 64 * NW;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE * 2 * D];  // K0 K1 V0 V1
+  // Four separate tile slots (K0, K1, V0, V1): each pipelined step writes one
+  // K and one V slot with direct loads while it reads the other two, and the
+  // slot choice is a compile-time constant there, so the compiler can see
+  // that the in-flight loads never alias the reads.
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILE * 2 * D];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILE * 2 * D];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILE * 2 * D];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILE * 2 * D];
   __shared__ int s_key[DENSE ? 1 : LMAX];
   __shared__ int s_base[DENSE ? 1 : LMAX];
   __shared__ int s_lim[DENSE ? 1 : LMAX];
@@ -319,12 +328,11 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
   float m_ref = -INFINITY;  // running max of x for this row (shared by both lane halves)
   float l_part = 0.f;       // this lane's share of the weighted denominator
 
-  // LDS: two K slots then two V slots. K runs one tile ahead of V so that QK
-  // of tile t+1 overlaps the softmax of tile t.
-  constexpr int TB = TILE * 2 * D;  // bytes per K (or V) tile
-  BSA_LDS char* lds = (BSA_LDS char*)(smem);  // address-space cast of the shared array
-  BSA_LDS char* kslot[2] = {lds, lds + TB};
-  BSA_LDS char* vslot[2] = {lds + 2 * TB, lds + 3 * TB};
+  // K runs one tile ahead of V so that QK of tile t+1 overlaps the softmax of tile t.
+  BSA_LDS char* const K0 = (BSA_LDS char*)(k_lds0);  // address-space casts of the shared arrays
+  BSA_LDS char* const K1 = (BSA_LDS char*)(k_lds1);
+  BSA_LDS char* const V0 = (BSA_LDS char*)(v_lds0);
+  BSA_LDS char* const V1 = (BSA_LDS char*)(v_lds1);
   const LaneOffsets<D> LO = lane_offsets<D>(kh, lane);
   const int n_chunks = DENSE ? 1 : (a.L + LMAX - 1) / LMAX;
   for (int ck = 0; ck < n_chunks; ++ck) {
@@ -341,20 +349,26 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
     auto meta_of = [&](int t) { return tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, t, n_entries); };
 
     // prologue: K(0), V(0), K(1) in flight; S(0) = QK(0)
-    stage_one<D, NW, BK, PERM, false>(a, kb, kslot[0], meta_of(0), wave, lane);
-    stage_one<D, NW, BK, PERM, true>(a, vb, vslot[0], meta_of(0), wave, lane);
-    if (n_tiles > 1) stage_one<D, NW, BK, PERM, false>(a, kb, kslot[1], meta_of(1), wave, lane);
+    stage_one<D, NW, BK, PERM, false>(a, kb, K0, meta_of(0), wave, lane);
+    stage_one<D, NW, BK, PERM, true>(a, vb, V0, meta_of(0), wave, lane);
+    if (n_tiles > 1) stage_one<D, NW, BK, PERM, false>(a, kb, K1, meta_of(1), wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 Sa[2], Sb[2];
-    qk_tile<D>(Sa, kslot[0], LO, qf);
+    qk_tile<D>(Sa, K0, LO, qf);
 
-    // One pipelined step: S_cur = QK(t) on entry, S_next = QK(t+1) on exit.
-    auto step = [&](f32x16 (&Scur)[2], f32x16 (&Snext)[2], int t) {
+    // One pipelined step: S_cur = QK(t) on entry, S_next = QK(t+1) on exit;
+    // PAR = t & 1 selects the slots at compile time.
+    auto step = [&](auto par_tag, f32x16 (&Scur)[2], f32x16 (&Snext)[2], int t) {
+      constexpr int PAR = decltype(par_tag)::value;
+      BSA_LDS char* const k_write = PAR ? K1 : K0;  // K(t+2) lands in K(t)'s slot
+      BSA_LDS char* const k_read = PAR ? K0 : K1;   // K(t+1)
+      BSA_LDS char* const v_write = PAR ? V0 : V1;  // V(t+1)
+      BSA_LDS char* const v_read = PAR ? V1 : V0;   // V(t)
       __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t+1) and V(t) loads have landed
       __syncthreads();                // ... everyone's; the K(t) and V(t-1) slots are free
-      if (t + 2 < n_tiles) stage_one<D, NW, BK, PERM, false>(a, kb, kslot[t & 1], meta_of(t + 2), wave, lane);
-      if (t + 1 < n_tiles) stage_one<D, NW, BK, PERM, true>(a, vb, vslot[(t + 1) & 1], meta_of(t + 1), wave, lane);
+      if (t + 2 < n_tiles) stage_one<D, NW, BK, PERM, false>(a, kb, k_write, meta_of(t + 2), wave, lane);
+      if (t + 1 < n_tiles) stage_one<D, NW, BK, PERM, true>(a, vb, v_write, meta_of(t + 1), wave, lane);
 
       // ---- branches first: mask, row max, lazy rescale of O ----
       const TileMeta mt = meta_of(t);
@@ -389,8 +403,8 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
       constexpr int NQ = D / 8;                // QK MFMAs per wave and tile
       constexpr int NP = 4 * (D / 32);         // PV MFMAs per wave and tile
       constexpr int PAIRS = 16 / NQ;           // softmax pairs per group (32 values per lane)
-      const BSA_LDS char* kn = kslot[(t + 1) & 1] + LO.kbase;
-      const BSA_LDS char* vt = vslot[t & 1] + LO.vbase;
+      const BSA_LDS char* kn = k_read + LO.kbase;
+      const BSA_LDS char* vt = v_read + LO.vbase;
       auto kread = [&](int i) {
         return *(const BSA_LDS u32x4*)(kn + 64 * D * (i % 2) + LO.koff[i / 2]);
       };
@@ -446,24 +460,26 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
 
     int t = 0;
     for (; t + 1 < n_tiles; t += 2) {
-      step(Sa, Sb, t);
-      step(Sb, Sa, t + 1);
+      step(std::integral_constant<int, 0>{}, Sa, Sb, t);
+      step(std::integral_constant<int, 1>{}, Sb, Sa, t + 1);
     }
-    if (t < n_tiles) step(Sa, Sb, t);
+    if (t < n_tiles) step(std::integral_constant<int, 0>{}, Sa, Sb, t);
   }
 
   // ---- merge the two key halves of each row group ----
   const float l_tot = halves_sum(l_part);
   __syncthreads();  // the tile buffers are free
-  static_assert(NRG * (D / 2 + 2) * 64 * 4 <= 4 * TILE * 2 * D, "merge area must fit the tile buffers");
-  float* part = reinterpret_cast<float*>(smem);         // [NRG][D/32 * 16][64]
-  float* pm = part + NRG * (D / 2) * 64;                 // [NRG][64]
+  // Partial O of row group rg: (D/2) x 64 floats = 128 D bytes; two row groups
+  // fit one tile slot (256 D bytes), so groups 0, 1 use k_lds0 and 2, 3 k_lds1.
+  static_assert(NRG <= 4, "at most four row groups");
+  float* part = reinterpret_cast<float*>(rg < 2 ? k_lds0 : k_lds1) + (rg % 2) * (D / 2) * 64;
+  float* pm = reinterpret_cast<float*>(v_lds0);          // [NRG][64]
   float* pl = pm + NRG * 64;
   if (kh == 1) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part[(rg * (D / 2) + dt * 16 + r) * 64 + lane] = o[dt][r];
+      for (int r = 0; r < 16; ++r) part[(dt * 16 + r) * 64 + lane] = o[dt][r];
     pm[rg * 64 + lane] = m_ref;
     pl[rg * 64 + lane] = l_tot;
   }
@@ -494,7 +510,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
 #pragma unroll
         for (int z = 0; z < 4; ++z) {
           const int r = 4 * g + z;
-          x[z] = (o[dt][r] * s0 + part[(rg * (D / 2) + dt * 16 + r) * 64 + lane] * s1) * inv;
+          x[z] = (o[dt][r] * s0 + part[(dt * 16 + r) * 64 + lane] * s1) * inv;
         }
         if constexpr (OUT32) {
           float* op = static_cast<float*>(a.out) + obase + col;
