@@ -23,11 +23,12 @@
 // row sum stay in the lane except for one exchange between 32-lane halves.
 //
 // Data movement. K and V tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4, no registers, no ALU work), double-buffered so the
-// next tile streams in while the current one is computed; both are stored
-// row-major with padded rows that keep the K reads (8 consecutive rows, one
-// 16-byte column) and the transposed V reads (4 consecutive rows, 32 bytes)
-// free of bank conflicts. The list of a query block is
+// (global_load_lds_dwordx4, no registers), double-buffered so the next tile
+// streams in while the current one is computed; both are stored row-major
+// with the 16-byte chunks of each row XOR-permuted so that the K reads and
+// the transposed V reads are free of bank conflicts. Each lane's share of a
+// staged tile sits at a fixed offset from the unit's first row, so a full
+// tile costs one address add per load. The list of a query block is
 // first rank-sorted by unit index so that concurrent workgroups sweep the keys
 // of a head in the same order, and workgroups are mapped so that all 8 XCDs
 // work on the same head at once, each on a contiguous run of query blocks.
@@ -102,33 +103,78 @@ struct TileMeta {
   int base[4];  // first global (pre-permutation) key row of each unit in the tile
   int lim[4];   // valid keys of each unit (0: empty slot or rejected entry)
   float lw[4];  // log2 of the unit's weight
+  bool full;    // every unit of the tile holds BK valid keys
 };
 
-// Direct global -> LDS staging of one 128-key tile of K or V. Each wave
-// instruction moves 1 KB = 1024 / (2 D) whole rows; lane l fills physical chunk
-// l % (D/8) of its row, i.e. logical chunk (l % (D/8)) ^ swz(row). Rows that are
-// not valid keys load a valid row of the same head (their logits are masked).
+__device__ __forceinline__ int pick4(const int (&x)[4], int u) {
+  return u == 0 ? x[0] : u == 1 ? x[1] : u == 2 ? x[2] : x[3];
+}
+
+// Direct global -> LDS staging of one 128-key tile of K or V. A wave
+// instruction moves 1 KB = RPI whole rows; lane l lands at byte 16 l of it,
+// i.e. in row l / CPR at physical chunk l % CPR, which holds logical chunk
+// (l % CPR) ^ swz(row). Instruction i of wave w covers tile rows
+// (i NW + w) RPI .. +RPI-1, so a lane's row is i G + r0 with G = NW RPI and
+// r0 = w RPI + l / CPR. G is a multiple of the swizzle periods, so the lane's
+// chunk and its byte offset r0 2D + 16 chunk are the same for every i and both
+// tensors' tiles: one per-lane register each for K and V, and the rest of the
+// address (the unit's first row, the instruction's row step) is uniform.
+// Rows of one instruction never straddle a unit (BK is a multiple of RPI).
+template <int D, int NW>
+struct StageGeom {
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int RPI = 1024 / (2 * D);   // rows per instruction
+  static constexpr int G = NW * RPI;           // row step between a wave's instructions
+  static constexpr int PER_WAVE = TILE / G;    // instructions per wave and tile
+  static_assert(G % 16 == 0 && TILE % G == 0, "swizzle periods must divide the row step");
+};
+
+template <int D, int NW>
+__device__ __forceinline__ uint32_t stage_lane_offset(int wave, int lane, bool is_v) {
+  using SG = StageGeom<D, NW>;
+  const int r0 = wave * SG::RPI + lane / SG::CPR;
+  return static_cast<uint32_t>(r0 * 2 * D + 16 * ((lane % SG::CPR) ^ (is_v ? v_swz<D>(r0) : k_swz<D>(r0))));
+}
+
+// swave: the wave index as a uniform value; lane_off: stage_lane_offset for this tensor.
 template <int D, int NW, int BK, bool PERM, bool IS_V>
 __device__ __forceinline__ void stage_one(const AttendArgs& a, const uint16_t* src, BSA_LDS char* dst,
-                                          const TileMeta& m, int wave, int lane) {
-  constexpr int CPR = D / 8;                   // chunks per row
-  constexpr int RPI = 1024 / (2 * D);          // rows per instruction
-  constexpr int PER_WAVE = TILE / RPI / NW;    // instructions per wave
-  static_assert(PER_WAVE * RPI * NW == TILE, "tile rows must split evenly over the waves");
+                                          const TileMeta& m, int swave, int lane, uint32_t lane_off) {
+  using SG = StageGeom<D, NW>;
+  if (!PERM && m.full) {
+    // every row valid: uniform base + the lane's fixed offset, no per-lane arithmetic
 #pragma unroll
-  for (int i = 0; i < PER_WAVE; ++i) {
-    const int ins = wave * PER_WAVE + i;
-    const int row = ins * RPI + lane / CPR;
-    const int u = (ins * RPI) / BK;  // rows of one instruction never straddle a unit
-    const int ubase = u == 0 ? m.base[0] : u == 1 ? m.base[1] : u == 2 ? m.base[2] : m.base[3];
-    const int ulim = u == 0 ? m.lim[0] : u == 1 ? m.lim[1] : u == 2 ? m.lim[2] : m.lim[3];
+    for (int i = 0; i < SG::PER_WAVE; ++i) {
+      const int row0 = i * SG::G + swave * SG::RPI;  // first tile row of the instruction
+      const int u = BK % SG::G == 0 ? i * SG::G / BK : row0 / BK;  // swave RPI < G
+      const int first = pick4(m.base, u) + i * SG::G - u * BK;  // key row of the lane with r0 = 0
+      const char* sp = reinterpret_cast<const char*>(src) + static_cast<size_t>(first) * (2 * D);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(sp + lane_off),
+                                       (BSA_LDS void*)(dst + (i * NW + swave) * 1024), 16, 0, 0);
+    }
+    return;
+  }
+  // partial or empty units, or a permutation: rows past a unit's valid keys load a
+  // valid row of the same head instead (their logits are masked).
+#pragma unroll
+  for (int i = 0; i < SG::PER_WAVE; ++i) {
+    const int row0 = i * SG::G + swave * SG::RPI;
+    const int u = BK % SG::G == 0 ? i * SG::G / BK : row0 / BK;
+    const int ubase = pick4(m.base, u);
+    const int ulim = pick4(m.lim, u);
+    const int row = row0 + lane / SG::CPR;
     const int o = row - u * BK;
-    bool ok = o < ulim;
-    int gr = gather_row<PERM>(a, ok ? ubase + o : ubase, ok);
-    if (!ok) gr = PERM ? 0 : ubase;  // any row of this head; masked later
-    const int lc = (lane % CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
+    int gr;
+    if constexpr (PERM) {
+      bool ok = o < ulim;
+      gr = gather_row<PERM>(a, ok ? ubase + o : ubase, ok);
+      if (!ok) gr = 0;  // any row of this head
+    } else {
+      gr = ubase + min(o, max(ulim, 1) - 1);  // an empty slot has base 0: row 0
+    }
+    const int lc = (lane % SG::CPR) ^ (IS_V ? v_swz<D>(row) : k_swz<D>(row));
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + static_cast<size_t>(gr) * D + lc * 8),
-                                     (BSA_LDS void*)(dst + ins * 1024), 16, 0, 0);
+                                     (BSA_LDS void*)(dst + (i * NW + swave) * 1024), 16, 0, 0);
   }
 }
 
@@ -173,6 +219,7 @@ __device__ __forceinline__ TileMeta tile_meta(const AttendArgs& a, const int* s_
     m.lim[u] = 0;
     m.lw[u] = 0.f;
   }
+  m.full = true;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if constexpr (DENSE) {
@@ -186,6 +233,7 @@ __device__ __forceinline__ TileMeta tile_meta(const AttendArgs& a, const int* s_
         m.lw[u] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_lw[e])));
       }
     }
+    m.full = m.full && m.lim[u] == BK;
   }
   return m;
 }
@@ -249,7 +297,9 @@ __device__ __forceinline__ void half_meta(const TileMeta& m, int kh, int (&lim)[
 }
 
 // Keys past the valid range of their unit get -inf (uniform branch; only
-// tiles that hold a partial or empty unit take it).
+// tiles that hold a partial or empty unit take it). Register r of sub-tile j
+// holds key off[j] + 8 (r/4) + 4 h + r%4 of its unit, so one per-lane
+// threshold lim - off - 4h is compared with a constant per register.
 template <int BK>
 __device__ __forceinline__ void mask_tile(f32x16 (&S)[2], const TileMeta& m, int kh, int h) {
   int lim[2], off[2];
@@ -257,10 +307,12 @@ __device__ __forceinline__ void mask_tile(f32x16 (&S)[2], const TileMeta& m, int
   half_meta<BK>(m, kh, lim, off, lw);
   if (off[0] + 32 > lim[0] || off[1] + 32 > lim[1]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const int thr = lim[j] - off[j] - 4 * h;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (off[j] + 8 * (r / 4) + 4 * h + (r % 4) >= lim[j]) S[j][r] = -INFINITY;
+        if (8 * (r / 4) + (r % 4) >= thr) S[j][r] = -INFINITY;
+    }
   }
 }
 
@@ -296,7 +348,8 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
   const int n = lane % 32, h = lane / 32;
-  const int rg = wave % NRG, kh = wave / NRG;
+  // wave-uniform indices held in scalar registers
+  const int rg = __builtin_amdgcn_readfirstlane(wave % NRG), kh = __builtin_amdgcn_readfirstlane(wave / NRG);
 
   // XCD-chunked mapping: hardware workgroup g runs on XCD g % 8; XCD x takes
   // query blocks [x*qchunk, (x+1)*qchunk) of each (b, h) in turn.
@@ -334,6 +387,9 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
   BSA_LDS char* const V0 = (BSA_LDS char*)(v_lds0);
   BSA_LDS char* const V1 = (BSA_LDS char*)(v_lds1);
   const LaneOffsets<D> LO = lane_offsets<D>(kh, lane);
+  const int swave = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t k_lane_off = stage_lane_offset<D, NW>(wave, lane, false);
+  const uint32_t v_lane_off = stage_lane_offset<D, NW>(wave, lane, true);
   const int n_chunks = DENSE ? 1 : (a.L + LMAX - 1) / LMAX;
   for (int ck = 0; ck < n_chunks; ++ck) {
     int n_entries = 0, n_tiles;
@@ -349,17 +405,20 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
     auto meta_of = [&](int t) { return tile_meta<BK, DENSE>(a, s_base, s_lim, s_lw, t, n_entries); };
 
     // prologue: K(0), V(0), K(1) in flight; S(0) = QK(0)
-    stage_one<D, NW, BK, PERM, false>(a, kb, K0, meta_of(0), wave, lane);
-    stage_one<D, NW, BK, PERM, true>(a, vb, V0, meta_of(0), wave, lane);
-    if (n_tiles > 1) stage_one<D, NW, BK, PERM, false>(a, kb, K1, meta_of(1), wave, lane);
+    const TileMeta meta0 = meta_of(0), meta1 = meta_of(1);
+    stage_one<D, NW, BK, PERM, false>(a, kb, K0, meta0, swave, lane, k_lane_off);
+    stage_one<D, NW, BK, PERM, true>(a, vb, V0, meta0, swave, lane, v_lane_off);
+    if (n_tiles > 1) stage_one<D, NW, BK, PERM, false>(a, kb, K1, meta1, swave, lane, k_lane_off);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 Sa[2], Sb[2];
     qk_tile<D>(Sa, K0, LO, qf);
 
     // One pipelined step: S_cur = QK(t) on entry, S_next = QK(t+1) on exit;
-    // PAR = t & 1 selects the slots at compile time.
-    auto step = [&](auto par_tag, f32x16 (&Scur)[2], f32x16 (&Snext)[2], int t) {
+    // PAR = t & 1 selects the slots at compile time. mt and mt1 describe tiles
+    // t and t+1; the step returns the description of tile t+2, which it stages.
+    auto step = [&](auto par_tag, f32x16 (&Scur)[2], f32x16 (&Snext)[2], int t, const TileMeta& mt,
+                    const TileMeta& mt1) -> TileMeta {
       constexpr int PAR = decltype(par_tag)::value;
       BSA_LDS char* const k_write = PAR ? K1 : K0;  // K(t+2) lands in K(t)'s slot
       BSA_LDS char* const k_read = PAR ? K0 : K1;   // K(t+1)
@@ -367,11 +426,11 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
       BSA_LDS char* const v_read = PAR ? V1 : V0;   // V(t)
       __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t+1) and V(t) loads have landed
       __syncthreads();                // ... everyone's; the K(t) and V(t-1) slots are free
-      if (t + 2 < n_tiles) stage_one<D, NW, BK, PERM, false>(a, kb, k_write, meta_of(t + 2), wave, lane);
-      if (t + 1 < n_tiles) stage_one<D, NW, BK, PERM, true>(a, vb, v_write, meta_of(t + 1), wave, lane);
+      const TileMeta mt2 = meta_of(t + 2);
+      if (t + 2 < n_tiles) stage_one<D, NW, BK, PERM, false>(a, kb, k_write, mt2, swave, lane, k_lane_off);
+      if (t + 1 < n_tiles) stage_one<D, NW, BK, PERM, true>(a, vb, v_write, mt1, swave, lane, v_lane_off);
 
       // ---- branches first: mask, row max, lazy rescale of O ----
-      const TileMeta mt = meta_of(t);
       mask_tile<BK>(Scur, mt, kh, h);
       int lim[2], off[2];
       float lw[2];
@@ -456,14 +515,18 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_bf16_kernel(AttendArgs a) {
         if (m + 4 < NP) vf[m % 4] = vread(m + 4);
         __builtin_amdgcn_sched_barrier(0);
       }
+      return mt2;
     };
 
     int t = 0;
+    TileMeta ma = meta0, mb = meta1;
     for (; t + 1 < n_tiles; t += 2) {
-      step(std::integral_constant<int, 0>{}, Sa, Sb, t);
-      step(std::integral_constant<int, 1>{}, Sb, Sa, t + 1);
+      const TileMeta mc = step(std::integral_constant<int, 0>{}, Sa, Sb, t, ma, mb);
+      const TileMeta md = step(std::integral_constant<int, 1>{}, Sb, Sa, t + 1, mb, mc);
+      ma = mc;
+      mb = md;
     }
-    if (t < n_tiles) step(std::integral_constant<int, 0>{}, Sa, Sb, t);
+    if (t < n_tiles) step(std::integral_constant<int, 0>{}, Sa, Sb, t, ma, mb);
   }
 
   // ---- merge the two key halves of each row group ----
