@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-ATTEND_SOURCE = os.path.join(ROOT, "block_sparse_attention_27_amd", "csrc", "attend_bf16.hpp")
+CSRC = os.path.join(ROOT, "block_sparse_attention_27_amd", "csrc")
 
 
 def _log(msg):
@@ -37,8 +37,13 @@ def _log(msg):
 
 
 def attend_source_hash() -> str:
-    with open(ATTEND_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the attention kernel sources (the attend_* headers and units, in name order)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.startswith("attend_") and name.endswith((".hpp", ".hip")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(workload: str):
