@@ -105,8 +105,23 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
     if (n_tiles > 1) stage_one<D, NW, BK, PERM, false>(a, kb, K1, meta1, swave, lane, k_lane_off);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // Running-max bookkeeping. When a tile's scores are complete, its maximum
+    // x decides the transition into it: rescale (need) when x exceeds the
+    // reference by more than the slack, to m_new, by alpha = 2^(m_ref - m_new).
+    // The transition is applied at the top of the step that computes the tile,
+    // after the previous tile's PV products have landed in O.
+    bool need = false;
+    float m_new = m_ref, alpha = 1.f;
+    auto decide = [&](float mx_lane) {
+      const float mx = halves_max(mx_lane) * a.c;  // c > 0
+      need = mx > m_ref + RESCALE_SLACK;
+      m_new = need ? mx : m_ref;
+      alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    };
     f32x16 Sa[2], Sb[2];
     qk_tile<D>(Sa, K0, LO, qf);
+    mask_tile<BK>(Sa, meta0, kh, h);
+    decide(tile_max(Sa));
 
     // One pipelined step: S_cur = QK(t) on entry, S_next = QK(t+1) on exit;
     // PAR = t & 1 selects the slots at compile time. mt and mt1 describe tiles
@@ -120,60 +135,8 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
       BSA_LDS char* const v_read = PAR ? V1 : V0;   // V(t)
       __builtin_amdgcn_s_waitcnt(0);  // this wave's K(t+1) and V(t) loads have landed
       __syncthreads();                // ... everyone's; the K(t) and V(t-1) slots are free
-      const TileMeta mt2 = meta_of(t + 2);
-      // Staging of K(t+2) and V(t+1). With a permutation (a gather per row)
-      // all of it happens here; otherwise one load per few MFMA groups below,
-      // branch-free: past the end of the list the loads fill the free slots
-      // with row 0 of the head, which nothing reads.
-      if constexpr (PERM) {
-        if (t + 2 < n_tiles) stage_one<D, NW, BK, PERM, false>(a, kb, k_write, mt2, swave, lane, k_lane_off);
-        if (t + 1 < n_tiles) stage_one<D, NW, BK, PERM, true>(a, vb, v_write, mt1, swave, lane, v_lane_off);
-      }
-      constexpr int PW = StageGeom<D, NW>::PER_WAVE;
-      // staging load k (K loads 0..PW-1, then V) goes with MFMA group k (NQ + NP) / (2 PW)
-      auto stage_k = [&](int grp) {
-        if constexpr (!PERM) {
-#pragma unroll
-          for (int k = 0; k < 2 * PW; ++k) {
-            if (k * (D / 8 + D / 8) / (2 * PW) != grp) continue;
-            if (k < PW) stage_ins<D, NW, BK>(kb, k_write, mt2, swave, st_r0, k_chunk, k);
-            else stage_ins<D, NW, BK>(vb, v_write, mt1, swave, st_r0, v_chunk, k - PW);
-          }
-        }
-      };
-
-      // ---- branches first: mask, row max, lazy rescale of O ----
-      mask_tile<BK>(Scur, mt, kh, h);
-      int lim[2], off[2];
-      float lw[2];
-      half_meta<BK>(mt, kh, lim, off, lw);
-      float mx = fmaxf(Scur[0][0], Scur[0][1]);
-#pragma unroll
-      for (int q2 = 1; q2 < 16; ++q2) {  // a chain of 3-input maxima over the 32 values
-        const int j = q2 / 8, r = 2 * (q2 % 8);
-        mx = fmaxf(mx, fmaxf(Scur[j][r], Scur[j][r + 1]));
-      }
-      mx = halves_max(mx) * a.c;  // c > 0
-      const bool need = mx > m_ref + RESCALE_SLACK;
-      const float m_new = need ? mx : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      }
-      l_part *= alpha;
-      m_ref = m_new;
-      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
-      const float bias0 = lw[0] - mb, bias1 = lw[1] - mb;
-
-      // ---- straight-line block, issued in this order (sched_barrier fences):
-      // group i = { QK(t+1) MFMA i, the K read four MFMAs ahead, softmax pair(s) of
-      // tile t }, then the PV(t) MFMAs with their transposed V reads four ahead.
-      constexpr int NQ = D / 8;                // QK MFMAs per wave and tile
-      constexpr int NP = 4 * (D / 32);         // PV MFMAs per wave and tile
-      constexpr int PAIRS = 16 / NQ;           // softmax pairs per group (32 values per lane)
+      // K reads for the first QK MFMAs go out first; the tile descriptions
+      // (LDS reads too) complete behind them
       const BSA_LDS char* kn = k_read + LO.kbase;
       const BSA_LDS char* vt = v_read + LO.vbase;
       auto kread = [&](int i) {
@@ -190,6 +153,51 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
       u32x4 kf[4], vf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) kf[i] = kread(i);
+      const TileMeta mt2 = meta_of(t + 2);
+      // Staging of K(t+2) and V(t+1). With a permutation (a gather per row)
+      // all of it happens here; otherwise one load per few MFMA groups below,
+      // branch-free: past the end of the list the loads fill the free slots
+      // with row 0 of the head, which nothing reads.
+      if constexpr (PERM) {
+        if (t + 2 < n_tiles) stage_one<D, NW, BK, PERM, false>(a, kb, k_write, mt2, swave, lane, k_lane_off);
+        if (t + 1 < n_tiles) stage_one<D, NW, BK, PERM, true>(a, vb, v_write, mt1, swave, lane, v_lane_off);
+      }
+      constexpr int PW = StageGeom<D, NW>::PER_WAVE;
+      // staging load k (K loads 0..PW-1, then V) goes with MFMA group 1 + k (NQ + NP) / (2 PW)
+      auto stage_k = [&](int grp) {
+        if constexpr (!PERM) {
+#pragma unroll
+          for (int k = 0; k < 2 * PW; ++k) {
+            if (1 + k * (D / 8 + D / 8) / (2 * PW) != grp) continue;
+            if (k < PW) stage_ins<D, NW, BK>(kb, k_write, mt2, swave, st_r0, k_chunk, k);
+            else stage_ins<D, NW, BK>(vb, v_write, mt1, swave, st_r0, v_chunk, k - PW);
+          }
+        }
+      };
+
+      // ---- tiles with keys past a unit's end: mask S(t) and redo its maximum
+      // (the previous step took it before masking); then the transition into t
+      if (mask_tile<BK>(Scur, mt, kh, h)) decide(tile_max(Scur));
+      if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      l_part *= alpha;
+      m_ref = m_new;
+      int lim[2], off[2];
+      float lw[2];
+      half_meta<BK>(mt, kh, lim, off, lw);
+      const float mb = (m_ref == -INFINITY) ? 0.f : m_ref;
+      const float bias0 = lw[0] - mb, bias1 = lw[1] - mb;
+
+      // ---- straight-line block, issued in this order (sched_barrier fences):
+      // group i = { QK(t+1) MFMA i, the K read four MFMAs ahead, softmax pair(s) of
+      // tile t }, then the PV(t) MFMAs with their transposed V reads four ahead.
+      constexpr int NQ = D / 8;                // QK MFMAs per wave and tile
+      constexpr int NP = 4 * (D / 32);         // PV MFMAs per wave and tile
+      constexpr int PAIRS = 16 / NQ;           // softmax pairs per group (32 values per lane)
       bf16x8 pb[4];
       float lsum = 0.f;
 #pragma unroll
@@ -220,13 +228,26 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
       // ---- O^T += V^T P^T over 4 steps of 16 keys of this wave's half. Step ks
       // takes P registers 8 (ks%2) + e of sub-tile ks/2, i.e. keys
       // 16 ks + 8 (e/4) + 4 h + e%4; the two transposed reads of vread fetch
-      // e = 0..3 and 4..7.
+      // e = 0..3 and 4..7. Alongside, the maximum of S(t+1) (16 steps of a
+      // 3-input maximum over groups 2 .. NP-2; before masking, which the next
+      // step applies if the tile needs it) and its transition decision.
+      float mx = -INFINITY;
+      constexpr int MS = NP - 3;
 #pragma unroll
       for (int m = 0; m < NP; ++m) {
         const int ks = m / (D / 32), dt = m % (D / 32);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[m % 4]), pb[ks], o[dt], 0, 0, 0);
         if (m + 4 < NP) vf[m % 4] = vread(m + 4);
         stage_k(NQ + m);
+        if (m >= 2 && m < NP - 1) {
+#pragma unroll
+          for (int q = (16 * (m - 2) + MS - 1) / MS; q < (16 * (m - 1) + MS - 1) / MS; ++q) {
+            mx = fmaxf(mx, fmaxf(Snext[q / 8][2 * (q % 8)], Snext[q / 8][2 * (q % 8) + 1]));
+            pin(mx);
+          }
+        } else if (m == NP - 1) {
+          decide(mx);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
       return mt2;
