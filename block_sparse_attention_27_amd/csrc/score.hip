@@ -14,8 +14,8 @@
 // accumulation, one LDS reduction per block). scores_kernel contracts the
 // fp32 means with v_mfma_f32_32x32x2_f32 in the S^T orientation (a lane holds
 // one query block, its registers 16 units), so each lane keeps its own
-// running max and n_j-weighted sum; pass 1 stores the raw logits into S and
-// pass 2 rewrites them normalised.
+// running max and n_j-weighted sum; a second pass recomputes the logits and
+// writes S once, normalised.
 #include "bsa_internal.hpp"
 
 #include <math.h>
@@ -114,15 +114,22 @@ struct ScoreArgs {
   float sm_scale;
 };
 
-constexpr int SC_WAVES = 4;
+constexpr int SC_WAVES = 8;
 
 // One workgroup per (b, h, group of 32 query blocks); wave w takes unit chunks
-// w, w + 4, ... (32 units each).
+// w, w + 8, ... (32 units each). Pass 1 contracts every chunk and keeps, per
+// lane (query block), the running maximum and n_j-weighted sum of
+// 2^(x - max) with x = l log2(e); the lane halves and the waves combine them.
+// Pass 2 contracts the chunks again (the means are small and stay in L2) and
+// writes the normalised scores once: each wave transposes its 32 x 32 block
+// through LDS so that every store instruction covers two contiguous 128-byte
+// row segments of S.
 template <int D>
 __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   constexpr int HALF = D / 2;  // lane half h contracts d in [h*HALF, (h+1)*HALF)
   __shared__ float red_m[SC_WAVES][32];
   __shared__ float red_s[SC_WAVES][32];
+  __shared__ float tile[SC_WAVES][32][33];  // one chunk of one wave: [query block][unit], padded
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int n = lane % 32, h = lane / 32;
@@ -138,12 +145,12 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     for (int y = 0; y < 4; ++y) qv[4 * z + y] = x[y];
   }
   const float* kmb = a.k_mean + static_cast<size_t>(bh) * a.nKU * D + h * HALF;
-  float* srow = a.S + (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * a.nKU;
   const int n_chunks = (a.nKU + 31) / 32;
-  const bool vec_ok = (a.nKU % 4) == 0;
+  const float c2 = a.sm_scale * 1.4426950408889634f;  // logits in log2 units
 
-  float run_m = -INFINITY, run_s = 0.f;
-  for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
+  // x for the 32 units of chunk ch: register r holds unit j0 + 8 (r/4) + 4 h + r%4;
+  // -inf for units with no valid key
+  auto logits = [&](int ch) {
     const int j0 = ch * 32;
     const int ja = j0 + n;  // A-operand row (unit) of this lane
     const bool aok = ja < a.nKU;
@@ -156,39 +163,33 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
       for (int y = 0; y < 4; ++y)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[y], qv[4 * z + y], acc, 0, 0, 0);
     }
-    // register r holds unit j0 + 8 (r/4) + 4 h + r%4
-    float lmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = j0 + 8 * (r / 4) + 4 * h + (r % 4);
       const bool valid = j < a.nKU && j * a.block_k < a.N;
-      acc[r] = valid ? acc[r] * a.sm_scale : -INFINITY;
-      lmax = fmaxf(lmax, acc[r]);
+      acc[r] = valid ? acc[r] * c2 : -INFINITY;
     }
+    return acc;
+  };
+  auto keys_of = [&](int j) { return static_cast<float>(max(0, min(a.block_k, a.N - j * a.block_k))); };
+
+  // ---- pass 1: running maximum and weighted sum per query block
+  float run_m = -INFINITY, run_s = 0.f;
+  for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
+    const f32x16 acc = logits(ch);
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, acc[r]);
     const float nm = fmaxf(run_m, lmax);
     if (nm != -INFINITY) {
-      float s = run_m == -INFINITY ? 0.f : run_s * expf(run_m - nm);
+      float s = run_m == -INFINITY ? 0.f : run_s * exp2f(run_m - nm);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 8 * (r / 4) + 4 * h + (r % 4);
-        const float nj = static_cast<float>(max(0, min(a.block_k, a.N - j * a.block_k)));
-        if (acc[r] != -INFINITY) s += nj * expf(acc[r] - nm);
+        const int j = ch * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+        if (acc[r] != -INFINITY) s += keys_of(j) * exp2f(acc[r] - nm);
       }
       run_s = s;
       run_m = nm;
-    }
-    if (qok) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = j0 + 8 * g + 4 * h;
-        if (vec_ok && j + 3 < a.nKU) {
-          *reinterpret_cast<f32x4*>(srow + j) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-        } else {
-#pragma unroll
-          for (int y = 0; y < 4; ++y)
-            if (j + y < a.nKU) srow[j + y] = acc[4 * g + y];
-        }
-      }
     }
   }
   // combine the two lane halves, then the waves
@@ -197,8 +198,8 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     const float nm = fmaxf(run_m, om);
     float s = 0.f;
     if (nm != -INFINITY) {
-      if (run_m != -INFINITY) s += run_s * expf(run_m - nm);
-      if (om != -INFINITY) s += os * expf(om - nm);
+      if (run_m != -INFINITY) s += run_s * exp2f(run_m - nm);
+      if (om != -INFINITY) s += os * exp2f(om - nm);
     }
     run_m = nm;
     run_s = s;
@@ -207,7 +208,6 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     red_m[wave][n] = run_m;
     red_s[wave][n] = run_s;
   }
-  __threadfence();  // pass-1 logits are visible before they are read back
   __syncthreads();
   float Lm = -INFINITY;
 #pragma unroll
@@ -215,35 +215,33 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   float Z = 0.f;
 #pragma unroll
   for (int x = 0; x < SC_WAVES; ++x)
-    if (red_m[x][n] != -INFINITY) Z += red_s[x][n] * expf(red_m[x][n] - Lm);
+    if (red_m[x][n] != -INFINITY) Z += red_s[x][n] * exp2f(red_m[x][n] - Lm);
   const float invZ = Z > 0.f ? 1.f / Z : 0.f;
 
-  if (!qok) return;
+  // ---- pass 2: normalised scores, written row-contiguously
+  float* sbase = a.S + (static_cast<size_t>(bh) * a.nQB + qg * 32) * a.nKU;
   for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
-    const int j0 = ch * 32;
+    const f32x16 acc = logits(ch);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int j = j0 + 8 * g + 4 * h;
-      if (vec_ok && j + 3 < a.nKU) {
-        f32x4 x = *reinterpret_cast<const f32x4*>(srow + j);
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int jj = j + y;
-          const float nj = static_cast<float>(max(0, min(a.block_k, a.N - jj * a.block_k)));
-          x[y] = nj > 0.f ? nj * expf(x[y] - Lm) * invZ : 0.f;
-        }
-        *reinterpret_cast<f32x4*>(srow + j) = x;
-      } else {
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int jj = j + y;
-          if (jj < a.nKU) {
-            const float nj = static_cast<float>(max(0, min(a.block_k, a.N - jj * a.block_k)));
-            srow[jj] = nj > 0.f ? nj * expf(srow[jj] - Lm) * invZ : 0.f;
-          }
-        }
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int jl = 8 * (r / 4) + 4 * h + (r % 4);
+      const float x = acc[r];
+      tile[wave][n][jl] = x == -INFINITY ? 0.f : keys_of(ch * 32 + jl) * exp2f(x - Lm) * invZ;
     }
+    // the block is exchanged between the lanes of this wave only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int col = ch * 32 + n;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int row = 2 * k + h;  // query block qg * 32 + row
+      if (qg * 32 + row < a.nQB && col < a.nKU) sbase[static_cast<size_t>(row) * a.nKU + col] = tile[wave][row][n];
+    }
+    // the next chunk's writes to the block wait for these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
