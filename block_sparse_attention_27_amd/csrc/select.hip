@@ -24,8 +24,10 @@
 // operations are two correctly rounded fp64 divisions and one fp64 -> fp32
 // rounding.
 //
-// Layout: thread t owns the E consecutive units [t E, t E + E), so block-wide
-// exclusive scans give ranks in unit order directly.
+// Layout: thread t owns the E consecutive units [t E, t E + E), so exclusive
+// scans give ranks in unit order directly. Rows of up to 1024 valid units take
+// one wave each (ballot counts, shuffle sums, no barriers); longer rows take a
+// 256-thread workgroup.
 #include "bsa_internal.hpp"
 
 namespace bsa {
@@ -322,6 +324,220 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   }
 }
 
+// ---- one wave per row (up to 64 E valid units) --------------------------
+// The same computation with every reduction inside one wave: counts from
+// ballots, sums and scans from lane shuffles, no workgroup barriers. Lane t
+// owns units [t E, t E + E).
+constexpr int SELW_WAVES = 4;
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(v, off)));
+  return v;
+}
+
+// Exclusive prefix over lanes; `total` receives the wave sum.
+__device__ __forceinline__ uint64_t wave_exscan(uint64_t v, uint64_t& total) {
+  const int lane = threadIdx.x % 64;
+  uint64_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  total = __shfl(x, 63);
+  return x - v;
+}
+
+template <int E>
+__global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs a, int rows) {
+  __shared__ uint32_t sbits[SELW_WAVES][64 * E];
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int row = blockIdx.x * SELW_WAVES + wave;
+  if (row >= rows) return;  // whole wave; nothing below synchronises across waves
+  const int i = row % a.nQB, bh = row / a.nQB;
+  const int hd = bh % a.H, b = bh / a.H;
+  const float* srow = a.S + static_cast<size_t>(row) * a.nKU;
+  const int L = a.k + a.m;
+  int32_t* irow = a.idx + static_cast<size_t>(row) * L;
+  float* wrow = a.w + static_cast<size_t>(row) * L;
+
+  uint32_t* sb = sbits[wave];
+  for (int x = lane; x < a.nV; x += 64) sb[x] = __float_as_uint(srow[x]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  uint32_t key[E];
+  bool valid[E], inK[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane * E + e;
+    const uint32_t raw = sb[j];  // inside the wave's slice; ignored past nV
+    valid[e] = j < a.nV;
+    key[e] = valid[e] ? sanitize(raw) : 0u;
+    inK[e] = false;
+  }
+
+  // ---- 1. exact set ----
+  if (a.k > 0) {
+    uint32_t T = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      uint32_t c = 0;  // cand >= 1, and invalid units hold key 0
+#pragma unroll
+      for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
+      if (c >= static_cast<uint32_t>(a.k)) T = cand;
+    }
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gt += __popcll(__ballot(valid[e] && key[e] > T));
+      eq += (valid[e] && key[e] == T) ? 1u : 0u;
+    }
+    const uint32_t need = static_cast<uint32_t>(a.k) - gt;
+    uint64_t eq_total;
+    uint32_t r = static_cast<uint32_t>(wave_exscan(eq, eq_total));
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!valid[e]) continue;
+      if (key[e] > T) {
+        inK[e] = true;
+      } else if (key[e] == T) {
+        inK[e] = r < need;
+        ++r;
+      }
+    }
+  }
+
+  bool inR[E], capped[E];
+  uint64_t pi[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    inR[e] = valid[e] && !inK[e];
+    capped[e] = false;
+    pi[e] = 0;
+  }
+
+  uint64_t delta = 0;
+  if (a.m > 0) {
+    // ---- 2a. quantised scores over R ----
+    uint32_t mx = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (inR[e]) mx = max(mx, key[e]);
+    mx = wave_max_u32(mx);
+    uint32_t q[E];
+    const int ex = mx ? frexp_exp(mx) : 0;
+    uint64_t qsum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      q[e] = inR[e] ? (mx ? quantise(key[e], ex) : 1u) : 0u;
+      qsum += q[e];
+    }
+    uint64_t QU = wave_sum(qsum);
+
+    // ---- 2b. water-filling on exact integers ----
+    uint64_t t = 0;
+    while (true) {
+      const uint64_t mt = static_cast<uint64_t>(a.m) - t;
+      uint64_t qcap = 0;
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool cap = inR[e] && !capped[e] && mt * q[e] >= QU;
+        cnt += __popcll(__ballot(cap));
+        if (cap) {
+          capped[e] = true;
+          qcap += q[e];
+        }
+      }
+      if (cnt == 0) break;
+      t += cnt;
+      QU -= wave_sum(qcap);
+    }
+
+    // ---- 2c. fixed-point pi ----
+    // (m - t) q_j < 2^33 and Q_U < 2^31 are exact in fp64, and so is their
+    // product form below; an uncapped unit has (m - t) q_j < Q_U, so its
+    // correctly rounded ratio is below 1 and 2^32 ratio fits 32 bits.
+    const uint64_t mt = static_cast<uint64_t>(a.m) - t;
+    const double mt_d = static_cast<double>(static_cast<uint32_t>(mt));
+    const double qu_d = static_cast<double>(QU);
+    uint64_t usum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!inR[e]) continue;
+      if (capped[e]) {
+        pi[e] = 1ull << 32;
+      } else {
+        const double ratio = (mt_d * static_cast<double>(q[e])) / qu_d;
+        pi[e] = static_cast<uint32_t>(ratio * 4294967296.0);
+        usum += pi[e];
+      }
+    }
+    delta = (mt << 32) - wave_sum(usum);
+  }
+
+  // ---- ranks in unit order: K (high word) and uncapped R (low word) ----
+  uint32_t nk = 0, nu = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    nk += inK[e] ? 1u : 0u;
+    nu += (inR[e] && !capped[e]) ? 1u : 0u;
+  }
+  uint64_t rk_total;
+  const uint64_t rk = wave_exscan((static_cast<uint64_t>(nk) << 32) | nu, rk_total);
+  uint32_t kpos = static_cast<uint32_t>(rk >> 32);
+  uint32_t upos = static_cast<uint32_t>(rk);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane * E + e;
+    if (inK[e]) {
+      irow[kpos] = j;
+      wrow[kpos] = 1.0f;
+      ++kpos;
+    }
+    if (a.m > 0 && inR[e] && !capped[e]) {
+      if (upos < delta) pi[e] += 1;
+      ++upos;
+    }
+  }
+
+  if (a.m > 0) {
+    // ---- 3. systematic sample over the cumulative pi axis ----
+    uint64_t psum = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) psum += pi[e];
+    uint64_t ptotal;
+    uint64_t c = wave_exscan(psum, ptotal);
+    const uint64_t u = philox_word0(static_cast<uint32_t>(i), static_cast<uint32_t>(hd),
+                                    static_cast<uint32_t>(b), 0u, a.seed_lo, a.seed_hi);
+    auto below = [u](uint64_t x) -> uint64_t { return x > u ? ((x - u - 1) >> 32) + 1 : 0; };
+    // every key is in registers now: the slice is reused to hand pi - 1 of
+    // each sampled slot (1 <= pi <= 2^32) to the lane that writes its weight
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!inR[e]) continue;
+      const uint64_t c0 = c;
+      c += pi[e];
+      const uint64_t n0 = below(c0), n1 = below(c);
+      if (n1 > n0 && n0 < static_cast<uint64_t>(a.m)) {  // k + m <= nV <= 64 E slots
+        irow[a.k + static_cast<int>(n0)] = lane * E + e;
+        sb[n0] = static_cast<uint32_t>(pi[e] - 1);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int x = lane; x < a.m; x += 64)
+      wrow[a.k + x] = static_cast<float>(4294967296.0 / (static_cast<double>(sb[x]) + 1.0));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_select(const Geometry& g, int k_exact, int m_sample, const float* S, int32_t* idx,
@@ -338,11 +554,20 @@ hipError_t launch_select(const Geometry& g, int k_exact, int m_sample, const flo
   a.m = m_sample;
   a.seed_lo = static_cast<uint32_t>(g.seed);
   a.seed_hi = static_cast<uint32_t>(g.seed >> 32);
-  const dim3 grid(g.B * g.H * g.nQB), block(SEL_THREADS);
-  if (a.nV <= SEL_THREADS) hipLaunchKernelGGL((select_kernel<1>), grid, block, 0, s, a);
-  else if (a.nV <= 2 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<2>), grid, block, 0, s, a);
-  else if (a.nV <= 4 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<4>), grid, block, 0, s, a);
-  else if (a.nV <= 8 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<8>), grid, block, 0, s, a);
+  const int rows = g.B * g.H * g.nQB;
+  const dim3 wgrid((rows + SELW_WAVES - 1) / SELW_WAVES), wblock(64 * SELW_WAVES);
+  const int per_lane = (a.nV + 63) / 64;
+  if (per_lane <= 16) {
+    if (per_lane <= 4) hipLaunchKernelGGL((select_wave_kernel<4>), wgrid, wblock, 0, s, a, rows);
+    else if (per_lane <= 6) hipLaunchKernelGGL((select_wave_kernel<6>), wgrid, wblock, 0, s, a, rows);
+    else if (per_lane <= 8) hipLaunchKernelGGL((select_wave_kernel<8>), wgrid, wblock, 0, s, a, rows);
+    else if (per_lane <= 10) hipLaunchKernelGGL((select_wave_kernel<10>), wgrid, wblock, 0, s, a, rows);
+    else if (per_lane <= 12) hipLaunchKernelGGL((select_wave_kernel<12>), wgrid, wblock, 0, s, a, rows);
+    else hipLaunchKernelGGL((select_wave_kernel<16>), wgrid, wblock, 0, s, a, rows);
+    return hipGetLastError();
+  }
+  const dim3 grid(rows), block(SEL_THREADS);
+  if (a.nV <= 8 * SEL_THREADS) hipLaunchKernelGGL((select_kernel<8>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((select_kernel<16>), grid, block, 0, s, a);
   return hipGetLastError();
 }
