@@ -7,7 +7,10 @@ blocks per query block, ~10% density). Inputs are resident in HBM before the
 timed region. The dense flash-attention kernel of the same library is timed
 separately for the speedup.
 
-Prints one JSON line. `value` is milliseconds per layer (lower is better);
+Prints one JSON line. `value` is milliseconds per layer (lower is better),
+warm: the timed steps run back to back. `cold` times each call on its own
+after 512 MB of writes have evicted the caches; `plan_reuse` times one
+score + select followed by r attend calls that reuse its lists.
 `roofline` describes bsa_attend (bf16 MFMA bound), timed with HIP events on
 the stream it runs on; `cpu_baseline` is the fp64 CPU oracle timed on a
 bounded sample of the same workload on this host's cores.
@@ -179,6 +182,38 @@ def main(argv=None):
     t_attend = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
     t_pass = statistics.mean(e[0].elapsed_time(e[3]) for e in evs)
 
+    # cold caches: 512 MB written before every call evicts L2 and the 256 MB
+    # Infinity Cache; each call is timed on its own
+    n_cold = max(3, min(args.steps, 5))
+    flush = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
+    cold = {"score": [], "select": [], "attend": []}
+    calls = (("score", lambda: bsa.bsa_score(p, q, k, perm, S, qm, km)),
+             ("select", lambda: bsa.bsa_select(p, S, idx, wt)),
+             ("attend", lambda: bsa.bsa_attend(p, q, k, v, perm, idx, wt, out, None)))
+    for _ in range(n_cold):
+        for name, call in calls:
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            cold[name].append((e0, e1))
+    torch.cuda.synchronize()
+    t_cold = {n: statistics.median(a.elapsed_time(b) for a, b in ev) for n, ev in cold.items()}
+    del flush
+
+    # sampling-plan reuse: one score + select, then r attend calls with that plan
+    reuse_r = 4
+    re = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    re[0].record(stream)
+    bsa.bsa_score(p, q, k, perm, S, qm, km)
+    bsa.bsa_select(p, S, idx, wt)
+    for _ in range(reuse_r):
+        bsa.bsa_attend(p, q, k, v, perm, idx, wt, out, None)
+    re[1].record(stream)
+    torch.cuda.synchronize()
+    t_reuse = re[0].elapsed_time(re[1]) / reuse_r
+
     # bsa_attend with a bf16 output, same lists
     out16 = torch.empty_like(q)
     be = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
@@ -249,6 +284,12 @@ def main(argv=None):
         "t_attend_bf16_out_ms": round(t_attend16, 4),
         "t_dense_ms": None if t_dense is None else round(t_dense, 4),
         "score_select_share": round((t_score + t_select) / t_pass, 4),
+        "cold": {"t_score_ms": round(t_cold["score"], 4), "t_select_ms": round(t_cold["select"], 4),
+                 "t_attend_ms": round(t_cold["attend"], 4),
+                 "t_pass_ms": round(sum(t_cold.values()), 4), "calls": n_cold,
+                 "flush": "512 MB written before every call"},
+        "plan_reuse": {"r": reuse_r, "ms_per_layer": round(t_reuse, 4),
+                       "score_select_share": round((t_score + t_select) / reuse_r / t_reuse, 4)},
         "executed_tflops": round(ach, 1),
         "executed_frac_peak": round(ach / PEAK_BF16_TFLOPS, 4),
         "dense_equiv_tflops": round(dense_flops / (t_pass * 1e-3) / 1e12, 1),

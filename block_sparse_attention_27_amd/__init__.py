@@ -12,7 +12,8 @@ in by the caller):
     bsa_attend(problem, q, k, v, perm, idx, w, out, lse)
     bsa_attend_dense(problem, q, k, v, perm, out, lse)
 Convenience wrappers that allocate their outputs: score, select, attend,
-attend_dense, sparse_attention (the three steps in order).
+attend_dense, sparse_attention (the three steps in order), and SamplingPlan,
+which keeps one score + select result for reuse by later attend calls.
 """
 
 from __future__ import annotations
@@ -26,7 +27,7 @@ from .inputs import Workload
 __all__ = [
     "Problem", "BsaError", "load_library", "library_path", "problem_for", "out_dtype",
     "bsa_score", "bsa_select", "bsa_attend", "bsa_attend_dense",
-    "score", "select", "attend", "attend_dense", "sparse_attention",
+    "score", "select", "attend", "attend_dense", "sparse_attention", "SamplingPlan",
     "BSA_OK", "BSA_ERR_INVALID_ARG", "BSA_ERR_UNSUPPORTED", "BSA_ERR_HIP", "BSA_BF16", "BSA_FP32",
 ]
 
@@ -255,3 +256,30 @@ def sparse_attention(p: Problem, q, k, v, perm=None, with_lse=False, stream=None
     idx, w = select(p, S, stream)
     res = attend(p, q, k, v, idx, w, perm, with_lse, stream)
     return (res if isinstance(res, tuple) else (res,)) + (idx, w)
+
+
+class SamplingPlan:
+    """One query-block sampling plan (idx, w), built once and reused.
+
+    AB-Attention (podcast transcript, the passage on reuse across nearby
+    denoising steps): the plan -- which key blocks each query block reads and
+    with what weight -- may be kept over nearby steps to save the selection
+    work, while attention itself is recomputed from each step's activations.
+    ``attend`` therefore runs only ``bsa_attend`` on the caller's current Q, K
+    and V with the stored lists; ``refresh`` rebuilds the plan (score, then
+    select) from new activations. The geometry (problem) is fixed per plan.
+    """
+
+    def __init__(self, p: Problem, q, k, perm=None, stream=None):
+        self.p = p
+        self.idx = None
+        self.w = None
+        self.refresh(q, k, perm, stream)
+
+    def refresh(self, q, k, perm=None, stream=None):
+        S, _, _ = score(self.p, q, k, perm, stream)
+        self.idx, self.w = select(self.p, S, stream)
+        return self
+
+    def attend(self, q, k, v, perm=None, with_lse=False, stream=None):
+        return attend(self.p, q, k, v, self.idx, self.w, perm, with_lse, stream)

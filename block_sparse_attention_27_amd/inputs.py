@@ -18,7 +18,10 @@ the layer shapes those models use:
   lower cluster id;
 * per (b, h) a centroid mu_c ~ N(0, 2^2 I_d) is drawn for every cluster;
   Q = (mu_c + e_q)/sqrt(d) and K = (mu_c + e_k)/sqrt(d) with independent
-  e ~ N(0, 0.5^2 I_d); V ~ N(0, 1);
+  e ~ N(0, 0.5^2 I_d); V ~ N(0, 1) (value_mode "noise", every preset), or
+  V = nu_c + e_v with a per-cluster value nu_c ~ N(0, I_d) and
+  e_v ~ N(0, 0.5^2 I_d) (value_mode "clustered": values that follow the
+  clusters, so that dense attention outputs are far from zero);
 * the logit scale is sm_scale = 1/temperature;
 * bf16 workloads are drawn in fp32 and rounded to nearest-even bf16;
 * the HunyuanVideo-shaped workload also carries a gather index that groups
@@ -28,7 +31,7 @@ the layer shapes those models use:
 Random streams: one numpy PCG64 stream seeded with ``[seed]`` draws the
 cluster seed points and the cluster relabelling; each (b, h) draws its
 centroids and noise from its own stream seeded with ``[seed, 1, b, h]``, so any
-head can be made alone.
+head can be made alone; clustered values draw nu_c from ``[seed, 2, b, h]``.
 """
 
 from __future__ import annotations
@@ -73,6 +76,7 @@ class Workload:
     centroid_std: float = 2.0
     seed: int = 0
     select_seed: int = 0
+    value_mode: str = "noise"  # "noise" or "clustered"
 
     @property
     def N(self) -> int:
@@ -222,6 +226,12 @@ def generate(w: Workload, heads: Optional[Iterable[int]] = None) -> dict:
                 x += base
                 x *= inv_sqrt_d
             out.append(x)
+        if w.value_mode == "clustered":
+            nu = np.random.default_rng([w.seed, 2, b, h]).standard_normal((w.clusters, d), dtype=np.float32)
+            out[2] *= np.float32(w.noise_std)
+            out[2] += nu[cid]
+        elif w.value_mode != "noise":
+            raise ValueError(f"unknown value_mode {w.value_mode!r}")
         for dst, x in zip((q, k, v), out):
             dst[b, hi, :N] = bf16_bits_from_f32(x) if bf16 else x
 

@@ -1,0 +1,39 @@
+"""The estimator study on the GPU: at the dense limit (k + m = every valid unit)
+every estimator must reproduce dense attention; below it every estimator gives
+a finite, positive error and the score mass of the best units lies in (0, 1]."""
+
+import math
+
+import pytest
+import torch
+
+from block_sparse_attention_27_amd.inputs import Workload
+from block_sparse_attention_27_amd.study import run_temperature
+from gpu_util import print_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(k, m, tau=1.0):
+    return Workload("study", B=1, H=2, grid=(3, 16, 24), d=128, dtype="bf16", block_q=128, block_k=128,
+                    k_exact=k, m_sample=m, clusters=6, temperature=tau)
+
+
+def test_study_dense_limit():
+    print_case("estimator study, k + m = all valid units")
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    w = _wl(2, 7)
+    assert w.list_len == w.n_valid_units
+    r = run_temperature(w, [0, 1], log=lambda m: None)
+    for name in ("truncation", "unweighted", "weighted", "sample_only"):
+        assert r[name] < 1e-4, (name, r[name])
+    assert abs(r["top_mass"] - 1.0) < 1e-5
+
+
+@pytest.mark.parametrize("tau", [0.5, 2.0])
+def test_study_sparse_finite(tau):
+    print_case(f"estimator study, k=1 m=3 tau={tau}")
+    r = run_temperature(_wl(1, 3, tau), [0, 1, 2], log=lambda m: None)
+    for name in ("truncation", "unweighted", "weighted", "sample_only"):
+        assert math.isfinite(r[name]) and r[name] > 0, (name, r[name])
+    assert 0 < r["top_mass"] <= 1 + 1e-6

@@ -1,10 +1,11 @@
 """Seeded workload generator: determinism, shapes, padding, bf16 rounding, permutation."""
 
 import numpy as np
+import pytest
 import torch
 
 from block_sparse_attention_27_amd.inputs import (WORKLOADS, generate, bf16_bits_from_f32,
-                                                  f32_from_bf16_bits, cluster_ids)
+                                                  f32_from_bf16_bits, cluster_ids, as_float32)
 
 
 def test_same_seed_same_bytes_and_head_subsets():
@@ -48,3 +49,17 @@ def test_headline_shape_numbers():
     assert abs(w.executed_flops() - 1.190e13) / 1.190e13 < 1e-3
     h = WORKLOADS["hunyuan"]
     assert (h.N_pad, h.n_units, h.n_valid_units, h.list_len * h.block_k) == (118912, 3716, 3713, 296 * 32)
+
+
+def test_clustered_values_follow_clusters_and_leave_q_k_alone():
+    w = WORKLOADS["tiny"].replace(grid=(2, 8, 8), clusters=4)
+    a, b = generate(w), generate(w.replace(value_mode="clustered"))
+    assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["k"], b["k"])
+    assert np.array_equal(b["v"], generate(w.replace(value_mode="clustered"))["v"])
+    cid = cluster_ids(w)
+    v = as_float32(b["v"])[0, 0, : w.N].astype(np.float64)
+    # the within-cluster spread is the value noise (std 0.5); the cluster means differ by ~N(0, 2)
+    within = np.mean([v[cid == c].std(axis=0).mean() for c in np.unique(cid) if (cid == c).sum() > 8])
+    assert 0.35 < within < 0.65
+    with pytest.raises(ValueError):
+        generate(w.replace(value_mode="other"))
