@@ -13,6 +13,8 @@ which holds none of the method's arithmetic.
 
 Modules, in the order the method runs:
   scoring    block means and the estimated-attention score matrix S
+  ibcs       the intra-block clustering scorer: k-means groups per query block,
+             S as the size-weighted mixture of the groups' estimated masses
   selection  exact top-k set, inclusion probabilities, systematic sample, 1/pi weights
   philox     the counter-based generator that supplies one offset per query block
   attention  weighted sparse attention, dense attention, and the two HT sums
@@ -25,6 +27,7 @@ rocRAND's host-callable Philox4x32-10).
 
 from .philox import philox4x32_10, philox4x32_10_np, block_offset
 from .scoring import apply_perm, unpermute, valid_counts, block_means, score
+from .ibcs import cluster_block, group_mixture, score_ibcs
 from .selection import (sanitize, exact_set, quantise, water_fill, fixed_point_pi,
                         systematic_sample, inverse_weight, select_row, select, F_BITS, FS_BITS)
 from .attention import (attend, attend_block, attend_dense, dense_block, dense_row_max,
@@ -33,6 +36,7 @@ from .attention import (attend, attend_block, attend_dense, dense_block, dense_r
 __all__ = [
     "philox4x32_10", "philox4x32_10_np", "block_offset",
     "apply_perm", "unpermute", "valid_counts", "block_means", "score",
+    "cluster_block", "group_mixture", "score_ibcs",
     "sanitize", "exact_set", "quantise", "water_fill", "fixed_point_pi",
     "systematic_sample", "inverse_weight", "select_row", "select", "F_BITS", "FS_BITS",
     "attend", "attend_block", "attend_dense", "dense_block", "dense_row_max",
