@@ -10,7 +10,8 @@ separately for the speedup.
 Prints one JSON line. `value` is milliseconds per layer (lower is better),
 warm: the timed steps run back to back. `cold` times each call on its own
 after 512 MB of writes have evicted the caches; `plan_reuse` times one
-score + select followed by r attend calls that reuse its lists.
+score + select followed by r attend calls that reuse its lists; `ibcs` times
+the intra-block clustering scorer in place of bsa_score.
 `roofline` describes bsa_attend (bf16 MFMA bound), timed with HIP events on
 the stream it runs on; `cpu_baseline` is the fp64 CPU oracle timed on a
 bounded sample of the same workload on this host's cores.
@@ -214,6 +215,21 @@ def main(argv=None):
     torch.cuda.synchronize()
     t_reuse = re[0].elapsed_time(re[1]) / reuse_r
 
+    # intra-block clustering scorer (4 groups, 3 k-means iterations) in place of bsa_score
+    ib_g, ib_t = 4, 3
+    qc = torch.empty((w.B, w.H, w.n_qblocks, ib_g, w.d), dtype=torch.float32, device="cuda")
+    qs = torch.empty((w.B, w.H, w.n_qblocks, ib_g), dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        bsa.bsa_score_ibcs(p, ib_g, ib_t, q, k, perm, S, qc, qs, km)
+    ie = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
+    for e in ie:
+        e[0].record(stream)
+        bsa.bsa_score_ibcs(p, ib_g, ib_t, q, k, perm, S, qc, qs, km)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t_ibcs = statistics.mean(e[0].elapsed_time(e[1]) for e in ie)
+    del qc, qs
+
     # bsa_attend with a bf16 output, same lists
     out16 = torch.empty_like(q)
     be = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
@@ -288,6 +304,8 @@ def main(argv=None):
                  "t_attend_ms": round(t_cold["attend"], 4),
                  "t_pass_ms": round(sum(t_cold.values()), 4), "calls": n_cold,
                  "flush": "512 MB written before every call"},
+        "ibcs": {"groups": ib_g, "iters": ib_t, "t_score_ms": round(t_ibcs, 4),
+                 "score_select_share": round((t_ibcs + t_select) / (t_ibcs + t_select + t_attend), 4)},
         "plan_reuse": {"r": reuse_r, "ms_per_layer": round(t_reuse, 4),
                        "score_select_share": round((t_score + t_select) / reuse_r / t_reuse, 4)},
         "executed_tflops": round(ach, 1),

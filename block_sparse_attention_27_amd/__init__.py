@@ -8,10 +8,11 @@ CPU fallback: if the library is missing, every call raises.
 Mirrors of the C entry points (same names and argument order, outputs passed
 in by the caller):
     bsa_score(problem, q, k, perm, S, q_mean, k_mean)
+    bsa_score_ibcs(problem, groups, iters, q, k, perm, S, q_cent, q_size, k_mean)
     bsa_select(problem, S, idx, w)
     bsa_attend(problem, q, k, v, perm, idx, w, out, lse)
     bsa_attend_dense(problem, q, k, v, perm, out, lse)
-Convenience wrappers that allocate their outputs: score, select, attend,
+Convenience wrappers that allocate their outputs: score, score_ibcs, select, attend,
 attend_dense, sparse_attention (the three steps in order), and SamplingPlan,
 which keeps one score + select result for reuse by later attend calls.
 """
@@ -26,8 +27,8 @@ from .inputs import Workload
 
 __all__ = [
     "Problem", "BsaError", "load_library", "library_path", "problem_for", "out_dtype",
-    "bsa_score", "bsa_select", "bsa_attend", "bsa_attend_dense",
-    "score", "select", "attend", "attend_dense", "sparse_attention", "SamplingPlan",
+    "bsa_score", "bsa_score_ibcs", "bsa_select", "bsa_attend", "bsa_attend_dense",
+    "score", "score_ibcs", "select", "attend", "attend_dense", "sparse_attention", "SamplingPlan",
     "BSA_OK", "BSA_ERR_INVALID_ARG", "BSA_ERR_UNSUPPORTED", "BSA_ERR_HIP", "BSA_BF16", "BSA_FP32",
 ]
 
@@ -91,6 +92,8 @@ def load_library():
     lib.bsa_status_string.argtypes = [ctypes.c_int32]
     lib.bsa_score.restype = ctypes.c_int
     lib.bsa_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsa_score_ibcs.restype = ctypes.c_int
+    lib.bsa_score_ibcs.argtypes = [P, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_select.restype = ctypes.c_int
     lib.bsa_select.argtypes = [P, vp, vp, vp, vp]
     lib.bsa_attend.restype = ctypes.c_int
@@ -172,6 +175,21 @@ def bsa_score(p: Problem, q, k, perm, S, q_mean, k_mean, stream=None):
                                                  _ptr(q_mean), _ptr(k_mean), _stream(stream)))
 
 
+def bsa_score_ibcs(p: Problem, groups: int, iters: int, q, k, perm, S, q_cent, q_size, k_mean, stream=None):
+    import torch
+    et = _elem_dtype(p)
+    _expect("q", q, (p.B, p.H, p.N_pad, p.d), et)
+    _expect("k", k, (p.B, p.H, p.N_pad, p.d), et)
+    _expect("perm", perm, (p.N_pad,), torch.int32)
+    _expect("S", S, (p.B, p.H, p.nQB, p.nKU), torch.float32)
+    _expect("q_cent", q_cent, (p.B, p.H, p.nQB, groups, p.d), torch.float32)
+    _expect("q_size", q_size, (p.B, p.H, p.nQB, groups), torch.int32)
+    _expect("k_mean", k_mean, (p.B, p.H, p.nKU, p.d), torch.float32)
+    _check("bsa_score_ibcs", load_library().bsa_score_ibcs(ctypes.byref(p), groups, iters, _ptr(q), _ptr(k),
+                                                           _ptr(perm), _ptr(S), _ptr(q_cent), _ptr(q_size),
+                                                           _ptr(k_mean), _stream(stream)))
+
+
 def bsa_select(p: Problem, S, idx, w, stream=None):
     import torch
     _expect("S", S, (p.B, p.H, p.nQB, p.nKU), torch.float32)
@@ -222,6 +240,18 @@ def score(p: Problem, q, k, perm=None, stream=None):
     km = torch.empty((p.B, p.H, p.nKU, p.d), dtype=torch.float32, device=dev)
     bsa_score(p, q, k, perm, S, qm, km, stream)
     return S, qm, km
+
+
+def score_ibcs(p: Problem, q, k, perm=None, groups: int = 4, iters: int = 3, stream=None):
+    """Returns (S, q_cent, q_size, k_mean)."""
+    import torch
+    dev = q.device
+    S = torch.empty((p.B, p.H, p.nQB, p.nKU), dtype=torch.float32, device=dev)
+    qc = torch.empty((p.B, p.H, p.nQB, groups, p.d), dtype=torch.float32, device=dev)
+    qs = torch.empty((p.B, p.H, p.nQB, groups), dtype=torch.int32, device=dev)
+    km = torch.empty((p.B, p.H, p.nKU, p.d), dtype=torch.float32, device=dev)
+    bsa_score_ibcs(p, groups, iters, q, k, perm, S, qc, qs, km, stream)
+    return S, qc, qs, km
 
 
 def select(p: Problem, S, stream=None):

@@ -8,7 +8,8 @@
 
 namespace {
 
-constexpr int kMaxSelectUnits = 4096;  // |valid units| * 2^20 must fit the 2^32 fixed point
+constexpr int kMaxSelectUnits = 4096;
+constexpr int kMaxClusterIters = 16;  // |valid units| * 2^20 must fit the 2^32 fixed point
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -94,9 +95,29 @@ bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const i
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(S, 4) || !aligned(q_mean, 16) || !aligned(k_mean, 16))
     return BSA_ERR_INVALID_ARG;
   if (perm && !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
-  st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, stream));
+  st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, false, stream));
   if (st != BSA_OK) return st;
-  return from_hip(bsa::launch_scores(g, q_mean, k_mean, S, stream));
+  return from_hip(bsa::launch_scores(g, 1, q_mean, nullptr, k_mean, S, stream));
+}
+
+bsa_status bsa_score_ibcs(const bsa_problem* p, int32_t groups, int32_t iters, const void* q, const void* k,
+                          const int32_t* perm, float* S, float* q_cent, int32_t* q_size, float* k_mean,
+                          hipStream_t stream) {
+  bsa::Geometry g;
+  bsa_status st = check_problem(p, &g);
+  if (st != BSA_OK) return st;
+  if (groups != 1 && groups != 2 && groups != 4 && groups != 8) return BSA_ERR_INVALID_ARG;
+  if (iters < 1 || iters > kMaxClusterIters) return BSA_ERR_INVALID_ARG;
+  if (!q || !k || !S || !q_cent || !q_size || !k_mean) return BSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(S, 4) || !aligned(q_cent, 16) || !aligned(q_size, 4) ||
+      !aligned(k_mean, 16))
+    return BSA_ERR_INVALID_ARG;
+  if (perm && !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
+  st = from_hip(bsa::launch_block_means(g, q, k, perm, nullptr, k_mean, true, stream));
+  if (st != BSA_OK) return st;
+  st = from_hip(bsa::launch_block_clusters(g, groups, iters, q, perm, q_cent, q_size, stream));
+  if (st != BSA_OK) return st;
+  return from_hip(bsa::launch_scores(g, groups, q_cent, q_size, k_mean, S, stream));
 }
 
 bsa_status bsa_select(const bsa_problem* p, const float* S, int32_t* idx, float* w, hipStream_t stream) {

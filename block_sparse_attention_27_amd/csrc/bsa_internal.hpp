@@ -17,10 +17,16 @@ struct Geometry {
 };
 
 // ---- scoring ----
+// keys_only: key-unit means only (q and q_mean unused)
 hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, const int32_t* perm,
-                              float* q_mean, float* k_mean, hipStream_t s);
-hipError_t launch_scores(const Geometry& g, const float* q_mean, const float* k_mean, float* S,
-                         hipStream_t s);
+                              float* q_mean, float* k_mean, bool keys_only, hipStream_t s);
+// groups in {1, 2, 4, 8}: q_rep holds `groups` representatives per query block,
+// q_size their row counts (nullptr with groups == 1: weight 1)
+hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, const int32_t* q_size,
+                         const float* k_mean, float* S, hipStream_t s);
+// k-means of every query block's valid rows: `groups` centroids and row counts
+hipError_t launch_block_clusters(const Geometry& g, int groups, int iters, const void* q,
+                                 const int32_t* perm, float* q_cent, int32_t* q_size, hipStream_t s);
 
 // ---- selection ----
 hipError_t launch_select(const Geometry& g, int k_exact, int m_sample, const float* S, int32_t* idx,

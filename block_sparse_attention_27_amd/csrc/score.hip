@@ -36,6 +36,7 @@ struct MeansArgs {
   float* q_mean;
   float* k_mean;
   int N, N_pad, block_q, block_k, nQB, nKU, n_bh;
+  int first;  // logical block of workgroup 0 (n_bh * nQB: key units only)
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
@@ -52,8 +53,9 @@ __global__ __launch_bounds__(MEAN_THREADS) void block_means_kernel(MeansArgs a) 
 
   const int tid = threadIdx.x;
   const int nq = a.n_bh * a.nQB;
-  const bool is_q = static_cast<int>(blockIdx.x) < nq;
-  const int blk = is_q ? blockIdx.x : blockIdx.x - nq;
+  const int lb = static_cast<int>(blockIdx.x) + a.first;
+  const bool is_q = lb < nq;
+  const int blk = is_q ? lb : lb - nq;
   const int per = is_q ? a.nQB : a.nKU;
   const int bs = is_q ? a.block_q : a.block_k;
   const int bh = blk / per, bi = blk % per;
@@ -107,7 +109,8 @@ __global__ __launch_bounds__(MEAN_THREADS) void block_means_kernel(MeansArgs a) 
 }
 
 struct ScoreArgs {
-  const float* q_mean;
+  const float* q_rep;     // [bh][nQB][G][D] query representatives (block means when G = 1)
+  const int32_t* q_size;  // [bh][nQB][G] rows per representative; nullptr: weight 1 (G = 1)
   const float* k_mean;
   float* S;
   int N, block_k, nQB, nKU, n_qgroups;
@@ -116,33 +119,51 @@ struct ScoreArgs {
 
 constexpr int SC_WAVES = 8;
 
-// One workgroup per (b, h, group of 32 query blocks); wave w takes unit chunks
-// w, w + 8, ... (32 units each). Pass 1 contracts every chunk and keeps, per
-// lane (query block), the running maximum and n_j-weighted sum of
+// One workgroup per (b, h, group of 32/G query blocks); wave w takes unit
+// chunks w, w + 8, ... (32 units each). MFMA column (lane) n holds
+// representative g = n % G of query block n / G. Pass 1 contracts every chunk
+// and keeps, per lane, the running maximum and n_j-weighted sum of
 // 2^(x - max) with x = l log2(e); the lane halves and the waves combine them.
-// Pass 2 contracts the chunks again (the means are small and stay in L2) and
-// writes the normalised scores once: each wave transposes its 32 x 32 block
-// through LDS so that every store instruction covers two contiguous 128-byte
-// row segments of S.
-template <int D>
+// Pass 2 contracts the chunks again (the representatives and key means are
+// small and stay in L2), scales every lane's normalised masses by its weight
+// n_g / n, sums the G lanes of a query block, and writes S once: each wave
+// transposes its block through LDS so that every store instruction covers two
+// contiguous 128-byte row segments of S.
+template <int D, int G>
 __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   constexpr int HALF = D / 2;  // lane half h contracts d in [h*HALF, (h+1)*HALF)
+  constexpr int QB = 32 / G;   // query blocks per workgroup
   __shared__ float red_m[SC_WAVES][32];
   __shared__ float red_s[SC_WAVES][32];
-  __shared__ float tile[SC_WAVES][32][33];  // one chunk of one wave: [query block][unit], padded
+  __shared__ float tile[SC_WAVES][QB][33];  // one chunk of one wave: [query block][unit], padded
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int n = lane % 32, h = lane / 32;
   const int bh = blockIdx.x / a.n_qgroups, qg = blockIdx.x % a.n_qgroups;
-  const int qb = qg * 32 + n;  // query block of this lane
+  const int ib = n / G, grp = n % G;
+  const int qb = qg * QB + ib;  // query block of this lane
   const bool qok = qb < a.nQB;
-  const float* qm = a.q_mean + (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * D + h * HALF;
+  const size_t rep = (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * G;
+  const float* qm = a.q_rep + (rep + grp) * D + h * HALF;
   float qv[HALF];
 #pragma unroll
   for (int z = 0; z < HALF / 4; ++z) {
     const f32x4 x = qok ? *reinterpret_cast<const f32x4*>(qm + 4 * z) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int y = 0; y < 4; ++y) qv[4 * z + y] = x[y];
+  }
+  // weight n_g / n of this lane's representative; a block with no valid row
+  // scores with its first (zero) representative alone
+  float wgt = 1.f;
+  if (a.q_size != nullptr) {
+    int tot = 0, mine = 0;
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+      const int c = qok ? a.q_size[rep + x] : 0;
+      tot += c;
+      mine = x == grp ? c : mine;
+    }
+    wgt = tot > 0 ? static_cast<float>(mine) / static_cast<float>(tot) : (grp == 0 ? 1.f : 0.f);
   }
   const float* kmb = a.k_mean + static_cast<size_t>(bh) * a.nKU * D + h * HALF;
   const int n_chunks = (a.nKU + 31) / 32;
@@ -219,14 +240,18 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   const float invZ = Z > 0.f ? 1.f / Z : 0.f;
 
   // ---- pass 2: normalised scores, written row-contiguously
-  float* sbase = a.S + (static_cast<size_t>(bh) * a.nQB + qg * 32) * a.nKU;
+  const float scale = invZ * wgt;
+  float* sbase = a.S + (static_cast<size_t>(bh) * a.nQB + qg * QB) * a.nKU;
   for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
     const f32x16 acc = logits(ch);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jl = 8 * (r / 4) + 4 * h + (r % 4);
       const float x = acc[r];
-      tile[wave][n][jl] = x == -INFINITY ? 0.f : keys_of(ch * 32 + jl) * exp2f(x - Lm) * invZ;
+      float v = x == -INFINITY ? 0.f : keys_of(ch * 32 + jl) * exp2f(x - Lm) * scale;
+#pragma unroll
+      for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off);  // the G lanes of one query block
+      if (grp == 0) tile[wave][ib][jl] = v;
     }
     // the block is exchanged between the lanes of this wave only
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -234,9 +259,9 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int col = ch * 32 + n;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int row = 2 * k + h;  // query block qg * 32 + row
-      if (qg * 32 + row < a.nQB && col < a.nKU) sbase[static_cast<size_t>(row) * a.nKU + col] = tile[wave][row][n];
+    for (int k = 0; k < QB / 2; ++k) {
+      const int row = 2 * k + h;  // query block qg * QB + row
+      if (qg * QB + row < a.nQB && col < a.nKU) sbase[static_cast<size_t>(row) * a.nKU + col] = tile[wave][row][n];
     }
     // the next chunk's writes to the block wait for these reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -248,7 +273,7 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
 }  // namespace
 
 hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, const int32_t* perm,
-                              float* q_mean, float* k_mean, hipStream_t s) {
+                              float* q_mean, float* k_mean, bool keys_only, hipStream_t s) {
   MeansArgs a;
   a.q = q;
   a.k = k;
@@ -262,7 +287,8 @@ hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, c
   a.nQB = g.nQB;
   a.nKU = g.nKU;
   a.n_bh = g.B * g.H;
-  const dim3 grid(a.n_bh * (g.nQB + g.nKU));
+  a.first = keys_only ? a.n_bh * g.nQB : 0;
+  const dim3 grid(a.n_bh * ((keys_only ? 0 : g.nQB) + g.nKU));
   const bool p = perm != nullptr;
 #define BSA_MEANS(D, BF, P) hipLaunchKernelGGL((block_means_kernel<D, BF, P>), grid, dim3(MEAN_THREADS), 0, s, a)
   if (g.d == 128) {
@@ -276,21 +302,37 @@ hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, c
   return hipGetLastError();
 }
 
-hipError_t launch_scores(const Geometry& g, const float* q_mean, const float* k_mean, float* S,
-                         hipStream_t s) {
+hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, const int32_t* q_size,
+                         const float* k_mean, float* S, hipStream_t s) {
   ScoreArgs a;
-  a.q_mean = q_mean;
+  a.q_rep = q_rep;
+  a.q_size = q_size;
   a.k_mean = k_mean;
   a.S = S;
   a.N = g.N;
   a.block_k = g.block_k;
   a.nQB = g.nQB;
   a.nKU = g.nKU;
-  a.n_qgroups = (g.nQB + 31) / 32;
+  const int per_wg = 32 / groups;
+  a.n_qgroups = (g.nQB + per_wg - 1) / per_wg;
   a.sm_scale = g.sm_scale;
-  const dim3 grid(g.B * g.H * a.n_qgroups);
-  if (g.d == 128) hipLaunchKernelGGL((scores_kernel<128>), grid, dim3(64 * SC_WAVES), 0, s, a);
-  else hipLaunchKernelGGL((scores_kernel<64>), grid, dim3(64 * SC_WAVES), 0, s, a);
+  const dim3 grid(g.B * g.H * a.n_qgroups), block(64 * SC_WAVES);
+#define BSA_SCORES(D, G) hipLaunchKernelGGL((scores_kernel<D, G>), grid, block, 0, s, a)
+#define BSA_SCORES_G(D)                      \
+  switch (groups) {                          \
+    case 1: BSA_SCORES(D, 1); break;         \
+    case 2: BSA_SCORES(D, 2); break;         \
+    case 4: BSA_SCORES(D, 4); break;         \
+    case 8: BSA_SCORES(D, 8); break;         \
+    default: return hipErrorInvalidValue;    \
+  }
+  if (g.d == 128) {
+    BSA_SCORES_G(128)
+  } else {
+    BSA_SCORES_G(64)
+  }
+#undef BSA_SCORES_G
+#undef BSA_SCORES
   return hipGetLastError();
 }
 

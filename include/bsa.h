@@ -11,8 +11,9 @@
  * attention pass in which every sampled block is reweighted by the inverse of
  * its inclusion probability in both the softmax numerator and denominator.
  *
- * Pipeline: bsa_score -> bsa_select -> bsa_attend. bsa_attend_dense is plain
- * dense attention built on the same tiling, for timing and checking.
+ * Pipeline: bsa_score (or bsa_score_ibcs) -> bsa_select -> bsa_attend.
+ * bsa_attend_dense is plain dense attention built on the same tiling, for
+ * timing and checking.
  *
  * Conventions shared by every call
  *   Layout     Q, K, V and out are contiguous row-major [B][H][N_pad][d]
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 2
+#define BSA_ABI_VERSION 3
 
 typedef enum bsa_status {
   BSA_OK = 0,
@@ -106,6 +107,35 @@ const char* bsa_status_string(int32_t status);
  */
 bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const int32_t* perm,
                      float* S, float* q_mean, float* k_mean, hipStream_t stream);
+
+/*
+ * bsa_score_ibcs -- the same score matrix from several representatives per
+ * query block: intra-block query clustering. (AB-Attention, Abstract: the
+ * Intra-Block Clustering Selector clusters queries only within each query
+ * block, without permuting tokens; transcript, the passage on choosing
+ * blocks: every group of similar queries gets a representative and a weight
+ * from its size, and the representatives score the key blocks.)
+ *
+ * Per query block with n > 0 valid rows, Lloyd's k-means with `groups`
+ * groups and `iters` iterations: initial centroid g = row floor(g n / groups)
+ * of the block (after the optional gather); each iteration assigns every row
+ * to its nearest centroid in squared Euclidean distance (ties: lower group)
+ * and moves every centroid to the mean of its rows (an empty group keeps its
+ * centroid). Then
+ *   S[b,h,i,j] = sum_g (n_g / n) n_j exp(l_gj) / sum_{valid j'} n_j' exp(l_gj'),
+ *       l_gj = sm_scale <q_cent_ig, k_mean_j>;  S = 0 for invalid units.
+ * A query block with no valid row scores like bsa_score's (one zero
+ * representative, weight 1) and reports zero centroids and sizes. With
+ * groups = 1 the result is bsa_score's. Distances and sums are fp32, so a row
+ * whose two nearest centroids are within fp32 rounding may join either.
+ *   groups    1, 2, 4 or 8;  iters  1..16 (else BSA_ERR_INVALID_ARG)
+ *   q_cent    [B][H][nQB][groups][d] fp32, out (16-byte aligned)
+ *   q_size    [B][H][nQB][groups] int32, out: rows per group, n_g
+ *   k_mean    [B][H][nKU][d] fp32, out, as in bsa_score
+ */
+bsa_status bsa_score_ibcs(const bsa_problem* p, int32_t groups, int32_t iters, const void* q, const void* k,
+                          const int32_t* perm, float* S, float* q_cent, int32_t* q_size, float* k_mean,
+                          hipStream_t stream);
 
 /*
  * bsa_select -- exact set plus fixed-size weighted sample, per (b, h, i).

@@ -15,61 +15,81 @@ readings taken here:
 
 * clustering is Lloyd's k-means with squared Euclidean distance on the query
   vectors of the block's n valid rows, G groups and T iterations;
-* the initial centroid of group g is row floor(g n / G) of the block (in the
-  block's own row order, after the optional permutation);
-* one iteration assigns every row to its nearest centroid (ties: the lower
-  group) and then replaces every centroid by the mean of its rows; a group
-  with no rows keeps its centroid;
-* the representative of group g is its final centroid c_g and its weight is
-  n_g / n, n_g being its row count after the last assignment;
+* the distances that decide the groups are exact integers: every row is
+  rounded to fixed point, q_int = rint(q 2^s) with s = 11 - e and e the
+  exponent of the block's largest magnitude (max |q| = f 2^e, f in [0.5, 1)),
+  so |q_int| <= 2^11 and a squared distance over d <= 128 dimensions is at
+  most 2^31 (an exact unsigned 32-bit sum); rounding is to nearest, ties to
+  even. The assignment is then a
+  decision that any implementation reproduces exactly;
+* the initial centroid of group g is q_int of row floor(g n / G) of the block
+  (in the block's own row order, after the optional permutation);
+* one iteration assigns every row to the nearest centroid (ties: the lower
+  group) and then replaces every centroid by the rounded mean of its rows,
+  floor((2 sum + n_g) / (2 n_g)) per dimension; a group with no rows keeps its
+  centroid;
+* the representative of group g is the mean of its member rows' original
+  values after the last assignment, its weight n_g / n; an empty group has the
+  zero representative and weight 0;
 * S[i, j] = sum_g (n_g / n) n_j exp(l_gj - L_g) / sum_{j' in V} n_j' exp(l_gj' - L_g)
   with l_gj = sm_scale <c_g, k_bar_j> and L_g = max_{j in V} l_gj: the mixture,
   by group size, of every group's estimated attention mass. Rows still sum to
   1 and S = 0 for units with no valid key;
 * a query block with no valid row scores like the plain scorer's empty block:
-  one group with the zero centroid and weight 1 (its sizes are all 0).
+  one group with the zero representative and weight 1 (its sizes are all 0).
 
-With G = 1 the one centroid is the block mean, so this is the plain scorer.
+With G = 1 the one representative is the block mean, so this is the plain
+scorer.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
 from .scoring import apply_perm, block_means, valid_counts
 
 
-def cluster_block(rows: np.ndarray, groups: int, iters: int):
+FIXED_BITS = 11  # |q_int| <= 2^11: d <= 128 squared differences sum to at most 2^31
+
+
+def fixed_point(rows: np.ndarray):
+    """Block rows -> (q_int int64, s): q_int = rint(rows 2^s), s = 11 - e(max |rows|)."""
+    mx = float(np.abs(rows).max()) if rows.size else 0.0
+    s = FIXED_BITS - math.frexp(mx)[1] if mx > 0 else 0
+    return np.rint(np.ldexp(rows, s)).astype(np.int64), s
+
+
+def cluster_block(rows: np.ndarray, groups: int, iters: int, history: bool = False):
     """k-means of one block's valid rows ([n, d], n >= 1) into ``groups`` groups.
 
-    Returns (centroids [G, d] fp64, sizes int64 [G], margin). ``margin`` is the
-    smallest relative gap (d2 - d1) / (d2 + d1) seen in any assignment between
-    a row's nearest centroid (d1) and the nearest centroid that differs from it
-    (d2); inf when every assignment was between identical centroids. A small
-    margin marks a near tie that a lower-precision computation may resolve
-    the other way.
+    Returns (representatives [G, d] fp64, sizes int64 [G]); with ``history``
+    also the fixed-point centroids after every iteration and the block's q_int.
     """
     rows = np.asarray(rows, dtype=np.float64)
     n = rows.shape[0]
-    c = rows[[(g * n) // groups for g in range(groups)]].copy()
-    margin = np.inf
+    qi, _ = fixed_point(rows)
+    c = qi[[(g * n) // groups for g in range(groups)]].copy()
     lab = np.zeros(n, dtype=np.int64)
+    hist = []
     for _ in range(iters):
-        d2 = ((rows[:, None, :] - c[None, :, :]) ** 2).sum(axis=-1)  # [n, G]
+        d2 = ((qi[:, None, :] - c[None, :, :]) ** 2).sum(axis=-1)  # [n, G], exact integers
         lab = np.argmin(d2, axis=1)  # first minimum: the lower group on ties
-        same = np.all(c[:, None, :] == c[None, :, :], axis=-1)     # [G, G] identical centroids
-        best = d2[np.arange(n), lab]
-        other = np.where(same[lab], np.inf, d2)
-        second = other.min(axis=1)
-        fin = np.isfinite(second)
-        if fin.any():
-            margin = min(margin, float(((second[fin] - best[fin]) / (second[fin] + best[fin])).min()))
         for g in range(groups):
-            members = rows[lab == g]
-            if members.shape[0]:
-                c[g] = members.sum(axis=0) / members.shape[0]
+            members = qi[lab == g]
+            ng = members.shape[0]
+            if ng:
+                c[g] = (2 * members.sum(axis=0) + ng) // (2 * ng)  # floor division: round half up
+        hist.append(c.copy())
     sizes = np.bincount(lab, minlength=groups).astype(np.int64)
-    return c, sizes, margin
+    reps = np.zeros((groups, rows.shape[1]))
+    for g in range(groups):
+        if sizes[g]:
+            reps[g] = rows[lab == g].sum(axis=0) / sizes[g]
+    if history:
+        return reps, sizes, hist, qi
+    return reps, sizes
 
 
 def group_mixture(cent: np.ndarray, weights: np.ndarray, k_bar: np.ndarray, n_j: np.ndarray,
@@ -90,10 +110,10 @@ def score_ibcs(q, k, N: int, block_q: int, block_k: int, sm_scale: float, groups
                perm=None, blocks=None):
     """IBCS score matrix.
 
-    With ``blocks`` None: returns (S float32 [B, H, nQB, nKU], centroids fp64
-    [B, H, nQB, G, d], sizes int64 [B, H, nQB, G], margins [B, H, nQB], k_bar).
-    With ``blocks`` a list of (b, h, i): the same quantities for those query
-    blocks only, as lists in that order (S rows, centroids, sizes, margins).
+    With ``blocks`` None: returns (S float32 [B, H, nQB, nKU], representatives
+    fp64 [B, H, nQB, G, d], sizes int64 [B, H, nQB, G], k_bar). With ``blocks``
+    a list of (b, h, i): the same quantities for those query blocks only, as
+    lists in that order (S rows, representatives, sizes).
     """
     qp = apply_perm(np.asarray(q, dtype=np.float64), perm)
     k_bar = block_means(k, N, block_k, perm)
@@ -105,25 +125,22 @@ def score_ibcs(q, k, N: int, block_q: int, block_k: int, sm_scale: float, groups
     def one(b, h, i):
         n = int(counts[i])
         if n == 0:
-            cent = np.zeros((groups, d))
+            reps = np.zeros((groups, d))
             sizes = np.zeros(groups, dtype=np.int64)
-            row = group_mixture(cent[:1], np.ones(1), k_bar[b, h], n_j, sm_scale)
-            return row, cent, sizes, np.inf
-        rows = qp[b, h, i * block_q: i * block_q + n]
-        cent, sizes, margin = cluster_block(rows, groups, iters)
-        row = group_mixture(cent, sizes / n, k_bar[b, h], n_j, sm_scale)
-        return row, cent, sizes, margin
+            row = group_mixture(reps[:1], np.ones(1), k_bar[b, h], n_j, sm_scale)
+            return row, reps, sizes
+        reps, sizes = cluster_block(qp[b, h, i * block_q: i * block_q + n], groups, iters)
+        row = group_mixture(reps, sizes / n, k_bar[b, h], n_j, sm_scale)
+        return row, reps, sizes
 
     if blocks is not None:
         res = [one(b, h, i) for (b, h, i) in blocks]
-        return ([r[0].astype(np.float32) for r in res], [r[1] for r in res], [r[2] for r in res],
-                [r[3] for r in res])
+        return [r[0].astype(np.float32) for r in res], [r[1] for r in res], [r[2] for r in res]
     S = np.zeros((B, H, nQB, k_bar.shape[2]), dtype=np.float64)
-    cents = np.zeros((B, H, nQB, groups, d))
+    reps = np.zeros((B, H, nQB, groups, d))
     sizes = np.zeros((B, H, nQB, groups), dtype=np.int64)
-    margins = np.zeros((B, H, nQB))
     for b in range(B):
         for h in range(H):
             for i in range(nQB):
-                S[b, h, i], cents[b, h, i], sizes[b, h, i], margins[b, h, i] = one(b, h, i)
-    return S.astype(np.float32), cents, sizes, margins, k_bar
+                S[b, h, i], reps[b, h, i], sizes[b, h, i] = one(b, h, i)
+    return S.astype(np.float32), reps, sizes, k_bar

@@ -32,8 +32,8 @@ def _declared_functions():
 
 def test_header_declares_the_pipeline():
     names = _declared_functions()
-    for n in ("bsa_score", "bsa_select", "bsa_attend", "bsa_attend_dense", "bsa_status_string",
-              "bsa_abi_version"):
+    for n in ("bsa_score", "bsa_score_ibcs", "bsa_select", "bsa_attend", "bsa_attend_dense",
+              "bsa_status_string", "bsa_abi_version"):
         assert n in names
 
 
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 2
+    assert lib.bsa_abi_version() == 3
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(1) == b"invalid argument"
     assert lib.bsa_status_string(99) == b"unknown status"
@@ -96,9 +96,27 @@ FAKE = ctypes.c_void_p(0x7F0000000000)  # never dereferenced: validation fails f
 def test_invalid_problem_rejected_by_every_call(lib, bad):
     p = ctypes.byref(_good(**bad))
     assert lib.bsa_score(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_score_ibcs(p, 4, 3, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_select(p, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_attend(p, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_attend_dense(p, FAKE, FAKE, FAKE, None, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("groups,iters", [(0, 3), (3, 3), (16, 3), (-1, 3), (4, 0), (4, 17), (4, -2)])
+def test_ibcs_groups_and_iterations_checked(lib, groups, iters):
+    p = ctypes.byref(_good())
+    assert lib.bsa_score_ibcs(p, groups, iters, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+                              None) == bsa.BSA_ERR_INVALID_ARG
+
+
+def test_ibcs_null_and_misaligned_outputs_rejected(lib):
+    p = ctypes.byref(_good())
+    bad4 = ctypes.c_void_p(0x7F0000000002)
+    odd = ctypes.c_void_p(0x7F0000000008)
+    for args in ((None, FAKE, FAKE, FAKE), (FAKE, None, FAKE, FAKE), (FAKE, FAKE, None, FAKE),
+                 (FAKE, FAKE, FAKE, None), (FAKE, odd, FAKE, FAKE), (FAKE, FAKE, bad4, FAKE),
+                 (FAKE, FAKE, FAKE, odd)):
+        assert lib.bsa_score_ibcs(p, 4, 3, FAKE, FAKE, None, *args, None) == bsa.BSA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("bad", BAD_BUDGET)

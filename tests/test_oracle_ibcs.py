@@ -1,15 +1,15 @@
 """Pins for the oracle's intra-block clustering scorer (CPU only): the one-group
 case against the plain scorer, exact two-cluster blocks against a direct
-softmax mixture, tie and empty-group handling worked by hand, Lloyd iterations
-against scikit-learn's KMeans, the monotone k-means cost, and the invariants of
-the full score matrix."""
+softmax mixture, tie and empty-group handling worked by hand, the fixed-point
+rounding rule, Lloyd iterations against scikit-learn's KMeans, the k-means
+cost bound of rounded centroids, and the invariants of the full score matrix."""
 
 import numpy as np
 import pytest
 from scipy.special import softmax
 
 from oracle import score, valid_counts
-from oracle.ibcs import cluster_block, group_mixture, score_ibcs
+from oracle.ibcs import cluster_block, fixed_point, group_mixture, score_ibcs
 
 
 def _tiny(seed=0, B=1, H=2, N=300, N_pad=384, d=16):
@@ -24,15 +24,31 @@ def _tiny(seed=0, B=1, H=2, N=300, N_pad=384, d=16):
 @pytest.mark.parametrize("iters", [1, 3])
 def test_one_group_is_the_plain_scorer(iters):
     q, k = _tiny()
-    perm = np.random.default_rng(5).permutation(384).astype(np.int32)
-    perm[300:] = np.arange(300, 384)
+    perm = np.arange(384, dtype=np.int32)
     perm[:300] = np.random.default_rng(6).permutation(300)
     for p in (None, perm):
-        S, cent, sizes, _, _ = score_ibcs(q, k, 300, 64, 32, 0.9, 1, iters, p)
+        S, reps, sizes, _ = score_ibcs(q, k, 300, 64, 32, 0.9, 1, iters, p)
         S0, qb, _ = score(q, k, 300, 64, 32, 0.9, p)
         assert np.allclose(S, S0, rtol=1e-6, atol=1e-9)
-        assert np.allclose(cent[:, :, :, 0, :], qb, rtol=1e-12, atol=1e-12)
+        assert np.allclose(reps[:, :, :, 0, :], qb, rtol=1e-12, atol=1e-12)
         assert np.array_equal(sizes[..., 0], np.broadcast_to(valid_counts(300, 384, 64), sizes[..., 0].shape))
+
+
+def test_fixed_point_rule():
+    rows = np.array([[0.75, -0.1], [0.3, 0.2]])        # max |q| = 0.75 = 0.75 * 2^0 -> s = 11
+    qi, s = fixed_point(rows)
+    assert s == 11 and qi.tolist() == [[1536, -205], [614, 410]]
+    qi, s = fixed_point(np.array([[3.0, 2.5, -1.0 / 4096]]))  # 3 = 0.75 * 2^2 -> s = 9
+    assert s == 9 and qi.tolist() == [[1536, 1280, 0]]
+    qi, s = fixed_point(np.array([[1.5 / 2048, 0.5 / 2048, 2.5 / 2048]]))  # 2.5/2048 -> e = -9, s = 20
+    assert s == 20 and qi.tolist() == [[768, 256, 1280]]
+    qi, s = fixed_point(np.array([[1.0, 0.5 ** 13, 3 * 0.5 ** 13]]))  # 1 = 0.5 * 2^1 -> s = 10: 0.125 -> 0, 0.375 -> 0
+    assert s == 10 and qi.tolist() == [[1024, 0, 0]]
+    qi, s = fixed_point(np.array([[1.0, 0.5 ** 11, 3 * 0.5 ** 11]]))  # halves round to even: 0.5 -> 0, 1.5 -> 2
+    assert qi.tolist() == [[1024, 0, 2]]
+    qi, s = fixed_point(np.zeros((2, 3)))
+    assert s == 0 and not qi.any()
+    assert np.abs(fixed_point(np.random.default_rng(0).standard_normal((128, 128)))[0]).max() <= 2048
 
 
 def _lattice(rng, d):
@@ -45,12 +61,11 @@ def test_two_exact_clusters_mixture():
     d, nku = 8, 6
     a, b = _lattice(rng, d), _lattice(rng, d)
     rows = np.array([a] * 60 + [b] * 68)
-    cent, sizes, margin = cluster_block(rows, 2, 1)   # initial rows 0 (a) and 64 (b)
-    assert np.array_equal(cent, np.array([a, b])) and list(sizes) == [60, 68]
-    assert margin > 0.01
+    reps, sizes = cluster_block(rows, 2, 1)   # initial rows 0 (a) and 64 (b)
+    assert np.array_equal(reps, np.array([a, b])) and list(sizes) == [60, 68]
     kb = rng.standard_normal((nku, d))
     n_j = np.array([32, 32, 32, 32, 17, 0], dtype=np.float64)
-    got = group_mixture(cent, sizes / 128, kb, n_j, 0.8)
+    got = group_mixture(reps, sizes / 128, kb, n_j, 0.8)
     logn = np.where(n_j > 0, np.log(np.maximum(n_j, 1)), -np.inf)
     want = 60 / 128 * softmax(0.8 * kb @ a + logn) + 68 / 128 * softmax(0.8 * kb @ b + logn)
     assert np.allclose(got, want, rtol=1e-13, atol=1e-15)
@@ -60,59 +75,66 @@ def test_two_exact_clusters_mixture():
 def test_duplicate_initial_centroids_and_an_empty_group():
     # rows 0..69 = a and 70..127 = b: both initial rows (0 and 64) are a, so the
     # first assignment is a tie everywhere and goes to group 0; group 1 is empty
-    # and keeps a. The second assignment splits a from b.
+    # (zero representative) but keeps its centroid a, so the second assignment
+    # splits a from b.
     rng = np.random.default_rng(2)
     d = 8
     a, b = _lattice(rng, d), _lattice(rng, d)
     while np.array_equal(a, b):
         b = _lattice(rng, d)
     rows = np.array([a] * 70 + [b] * 58)
-    c1, s1, m1 = cluster_block(rows, 2, 1)
+    r1, s1, hist, qi = cluster_block(rows, 2, 1, history=True)
     assert list(s1) == [128, 0]
-    assert np.array_equal(c1[1], a)
-    assert np.allclose(c1[0], (70 * a + 58 * b) / 128, rtol=0, atol=1e-15)
-    assert m1 == np.inf  # every first assignment compared two identical centroids
-    c2, s2, _ = cluster_block(rows, 2, 2)
+    assert not r1[1].any()
+    assert np.allclose(r1[0], (70 * a + 58 * b) / 128, rtol=0, atol=1e-15)
+    assert np.array_equal(hist[0][1], qi[0])          # the empty group kept its centroid
+    expect = (2 * (70 * qi[0] + 58 * qi[70]) + 128) // 256
+    assert np.array_equal(hist[0][0], expect)          # rounded mean, half up
+    r2, s2 = cluster_block(rows, 2, 2)
     assert list(s2) == [58, 70]
-    assert np.array_equal(c2, np.array([b, a]))
+    assert np.array_equal(r2, np.array([b, a]))
 
 
 def test_fewer_rows_than_groups():
     rows = np.array([[0.0, 1.0], [2.0, 0.0], [5.0, 5.0]])
     # initial rows floor(g * 3 / 4) = 0, 0, 1, 2: group 1 duplicates group 0 and stays empty
-    cent, sizes, _ = cluster_block(rows, 4, 3)
+    reps, sizes = cluster_block(rows, 4, 3)
     assert list(sizes) == [1, 0, 1, 1]
-    assert np.array_equal(cent, rows[[0, 0, 1, 2]])
+    assert np.array_equal(reps, np.array([rows[0], [0.0, 0.0], rows[1], rows[2]]))
 
 
 def test_lloyd_iterations_match_scikit_learn():
     KMeans = pytest.importorskip("sklearn.cluster").KMeans
-    rng = np.random.default_rng(3)
-    centres = rng.standard_normal((3, 16)) * 3
-    rows = centres[rng.integers(0, 3, 128)] + rng.standard_normal((128, 16))
-    for groups, iters in ((4, 1), (4, 2), (4, 5), (2, 3), (8, 4)):
-        cent, sizes, _ = cluster_block(rows, groups, iters)
+    for groups, iters in ((4, 1), (4, 2), (4, 5), (2, 3), (8, 4), (3, 6)):
+        rng = np.random.default_rng(100 + 10 * groups + iters)
+        centres = rng.standard_normal((groups, 16)) * 2
+        rows = centres[rng.integers(0, groups, 128)] + rng.standard_normal((128, 16))
+        qi, s = fixed_point(rows)
+        rows = np.ldexp(qi.astype(np.float64), -s)  # on the fixed-point grid: the same points for both
+        reps, sizes = cluster_block(rows, groups, iters)
         assert sizes.min() > 0  # scikit-learn relocates empty clusters; keep them out of the comparison
         init = rows[[(g * 128) // groups for g in range(groups)]]
         km = KMeans(n_clusters=groups, init=init, n_init=1, max_iter=iters, tol=0.0,
                     algorithm="lloyd").fit(rows)
-        assert np.allclose(cent, km.cluster_centers_, rtol=1e-9, atol=1e-9), (groups, iters)
+        # scikit-learn's centres are the means of its last assignment, as the representatives
+        # are; the rounded fixed-point centroids move no assignment on these rows
+        assert np.allclose(reps, km.cluster_centers_, rtol=1e-9, atol=1e-9), (groups, iters)
 
 
-def test_kmeans_cost_never_increases():
+def test_kmeans_cost_bound_with_rounded_centroids():
+    # Lloyd's cost cannot rise by more than the centroid rounding: at most n d / 4 per iteration
     rng = np.random.default_rng(4)
     rows = rng.standard_normal((128, 32)) + np.repeat(rng.standard_normal((4, 32)) * 2, 32, axis=0)
     rng.shuffle(rows)
-    cost = []
-    for iters in range(1, 8):
-        cent, _, _ = cluster_block(rows, 4, iters)
-        cost.append(((rows[:, None, :] - cent[None]) ** 2).sum(-1).min(axis=1).sum())
-    assert all(c2 <= c1 * (1 + 1e-12) for c1, c2 in zip(cost, cost[1:])), cost
+    _, _, hist, qi = cluster_block(rows, 4, 8, history=True)
+    cost = [int(((qi[:, None, :] - c[None]) ** 2).sum(-1).min(axis=1).sum()) for c in hist]
+    assert all(c2 <= c1 + 128 * 32 // 4 for c1, c2 in zip(cost, cost[1:])), cost
+    assert cost[-1] < cost[0]
 
 
 def test_score_matrix_invariants():
     q, k = _tiny(seed=7, N=300, N_pad=512)   # query blocks 5..7 of 64 rows hold no valid row
-    S, cent, sizes, margins, _ = score_ibcs(q, k, 300, 64, 32, 1.3, 4, 3)
+    S, reps, sizes, _ = score_ibcs(q, k, 300, 64, 32, 1.3, 4, 3)
     n_q = valid_counts(300, 512, 64)
     n_j = valid_counts(300, 512, 32)
     assert np.allclose(S.astype(np.float64).sum(-1), 1.0, atol=1e-6)
@@ -121,12 +143,13 @@ def test_score_matrix_invariants():
     # an empty query block scores like the plain scorer's empty block (zero mean: mass in proportion to n_j)
     S0, _, _ = score(q, k, 300, 64, 32, 1.3)
     assert np.allclose(S[:, :, 5:], S0[:, :, 5:], rtol=1e-6)
+    assert not reps[:, :, 5:].any()
     # more groups than one actually split these blocks
     assert np.all((sizes[:, :, :4] > 0).sum(-1) >= 2)
     # the subset form returns the same rows
-    rows, c_sub, s_sub, m_sub = score_ibcs(q, k, 300, 64, 32, 1.3, 4, 3, blocks=[(0, 1, 2), (0, 0, 6)])
+    rows, r_sub, s_sub = score_ibcs(q, k, 300, 64, 32, 1.3, 4, 3, blocks=[(0, 1, 2), (0, 0, 6)])
     assert np.array_equal(rows[0], S[0, 1, 2]) and np.array_equal(rows[1], S[0, 0, 6])
-    assert np.array_equal(s_sub[0], sizes[0, 1, 2]) and m_sub[0] == margins[0, 1, 2]
+    assert np.array_equal(s_sub[0], sizes[0, 1, 2]) and np.array_equal(r_sub[0], reps[0, 1, 2])
 
 
 def test_full_scorer_weights_groups_by_size():
@@ -140,7 +163,7 @@ def test_full_scorer_weights_groups_by_size():
     k = rng.standard_normal((1, 1, Np, d))
     k[..., N:, :] = 0
     q[..., N:, :] = 0
-    S, cent, sizes, _, _ = score_ibcs(q, k, N, 64, 32, 0.6, 2, 2)
+    S, reps, sizes, _ = score_ibcs(q, k, N, 64, 32, 0.6, 2, 2)
     assert list(sizes[0, 0, 0]) == [30, 34]
     n_j = np.array([min(32, max(0, N - 32 * j)) for j in range(Np // 32)], dtype=np.float64)
     kb = np.array([k[0, 0, 32 * j: 32 * j + int(n)].mean(axis=0) if n else np.zeros(d)
@@ -148,3 +171,17 @@ def test_full_scorer_weights_groups_by_size():
     logn = np.where(n_j > 0, np.log(np.maximum(n_j, 1)), -np.inf)
     want = 30 / 64 * softmax(0.6 * kb @ a + logn) + 34 / 64 * softmax(0.6 * kb @ b + logn)
     assert np.allclose(S[0, 0, 0], want, rtol=1e-6, atol=1e-9)
+
+
+def test_centroid_rounding_half_up():
+    # one group: the centroid after one iteration is the rounded mean of the fixed-point rows
+    rows = np.array([[1.0, 1.0 / 1024, -1.0], [1.0, 0.0, -1.0], [0.0, 0.0, 0.0]])
+    _, _, hist, qi = cluster_block(rows, 1, 1, history=True)
+    assert qi.tolist() == [[1024, 1, -1024], [1024, 0, -1024], [0, 0, 0]]
+    # means 682.67 -> 683, 0.33 -> 0, -682.67 -> -683
+    assert hist[0][0].tolist() == [683, 0, -683]
+    _, _, hist, _ = cluster_block(rows[:2], 1, 1, history=True)
+    # means 1024, 0.5 -> 1 (half up), -1024
+    assert hist[0][0].tolist() == [1024, 1, -1024]
+    _, _, hist, _ = cluster_block(-rows[:2], 1, 1, history=True)
+    assert hist[0][0].tolist() == [-1024, 0, 1024]  # -0.5 -> 0 (half up)
