@@ -29,9 +29,11 @@
 // staged once in LDS in their input type, next to their 16-bit fixed-point
 // copies. A distance is |q|^2 + |c|^2 - 2 <q, c> with the inner product on
 // v_dot2_i32_i16 (two dimensions per instruction, exact); TPR threads share a
-// row and every centroid read is an LDS broadcast. The centroid sums are
-// integer LDS atomics (exact, so their order does not matter); the final fp32
-// means use a fixed order, so the output is deterministic.
+// row and every centroid read is an LDS broadcast. For the centroid sums a
+// thread owns one column of a range of rows; all lanes of a wave walk the same
+// rows, so a row's group is wave-uniform and each row costs one add into the
+// right register. The final fp32 means use a fixed order, so the output is
+// deterministic.
 #include "bsa_internal.hpp"
 
 namespace bsa {
@@ -97,15 +99,15 @@ __global__ __launch_bounds__(CL_THREADS) void block_clusters_kernel(ClusterArgs 
   __shared__ __align__(16) T rows[BQ][LD];
   __shared__ __align__(16) short qi[BQ][LDI];  // fixed-point rows
   __shared__ __align__(16) short ci[G][D];     // fixed-point centroids
-  __shared__ int sums[G][D];                    // centroid sums (atomics)
   __shared__ int qq[BQ];                        // |q_int|^2 per row
-  __shared__ int ccp[TPR][G];                   // |c_int|^2 per distance part
+  __shared__ int cc2[G];                        // |c_int|^2 per centroid
   __shared__ union {
     int ip[NPART];       // partial inner products
     float fsum[NPART];   // partial sums of the original values
   } part;
-  __shared__ int lab[BQ];
-  __shared__ int cnt[G];
+  constexpr int NW = (BQ + 63) / 64;  // waves that hold rows in the assignment step
+  __shared__ int rowlist[BQ];         // rows ordered by group, ascending within a group
+  __shared__ int wcnt[NW][G];         // rows of each group per assignment wave
   __shared__ float wmax[CL_THREADS / 64];
 
   const int tid = threadIdx.x;
@@ -175,6 +177,22 @@ __global__ __launch_bounds__(CL_THREADS) void block_clusters_kernel(ClusterArgs 
   }
   __syncthreads();  // rows and fixed-point rows ready
   for (int x = tid; x < G * D; x += CL_THREADS) ci[x / D][x % D] = qi[((x / D) * n) / G][x % D];
+  if (tid < G) cc2[tid] = 0;
+  __syncthreads();
+  // |c_int|^2 of every centroid: column tid of each, summed per wave, then across waves
+  auto centroid_squares = [&]() {
+    if (tid < D) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int c = ci[g][tid];
+        int v = c * c;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (tid % 64 == 0) atomicAdd(&cc2[g], v);
+      }
+    }
+  };
+  centroid_squares();
 
   const int dr = tid % BQ, dp = tid / BQ;   // distance step: row dr, dimensions [dp DP, dp DP + DP)
   const int uj = tid % D, up = tid / D;     // sum steps: column uj, rows [up RP, up RP + RP)
@@ -198,101 +216,135 @@ __global__ __launch_bounds__(CL_THREADS) void block_clusters_kernel(ClusterArgs 
     qq[tid] = s;
   }
 
+  int cnt_s[G], off_s[G];  // group sizes and rowlist offsets of the last assignment
   for (int it = 0; it < a.iters; ++it) {
-    if (tid < G) cnt[tid] = 0;
-    for (int x = tid; x < G * D; x += CL_THREADS) sums[x / D][x % D] = 0;
-    __syncthreads();  // centroids and |q|^2 ready; counts and sums cleared
+    __syncthreads();  // centroids and |q|^2 ready
     {
-      int acc[G], cacc[G];
+      int acc[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] = cacc[g] = 0;
+      for (int g = 0; g < G; ++g) acc[g] = 0;
 #pragma unroll
       for (int e = 0; e < DP; e += 8) {
         const int j0 = dp * DP + e;
         const i32x4 x = *reinterpret_cast<const i32x4*>(&qi[dr][j0]);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const i32x4 c = *reinterpret_cast<const i32x4*>(&ci[g][j0]);  // broadcast
-          acc[g] = dot8(x, c, acc[g]);
-          cacc[g] = dot8(c, c, cacc[g]);
-        }
+        for (int g = 0; g < G; ++g) acc[g] = dot8(x, *reinterpret_cast<const i32x4*>(&ci[g][j0]), acc[g]);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) part.ip[(dp * BQ + dr) * G + g] = acc[g];
-      if (dr == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) ccp[dp][g] = cacc[g];
-      }
     }
     __syncthreads();  // partial inner products ready
-    if (tid < n) {
-      uint32_t best = 0u;
-      int bg = 0;
+    int myl = G, rank = 0;  // group of row tid (G: no row) and its rank among the wave's rows of that group
+    if (tid < 64 * NW) {    // whole waves
+      if (tid < n) {
+        uint32_t best = 0u;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        int ip = 0, cc = 0;
+        for (int g = 0; g < G; ++g) {
+          int ip = 0;
 #pragma unroll
-        for (int x = 0; x < TPR; ++x) {
-          ip += part.ip[(x * BQ + tid) * G + g];
-          cc += ccp[x][g];
-        }
-        // |q - c|^2 in [0, 2^31]: exact in unsigned 32-bit arithmetic
-        const uint32_t d2 = static_cast<uint32_t>(qq[tid]) + static_cast<uint32_t>(cc) - 2u * static_cast<uint32_t>(ip);
-        if (g == 0 || d2 < best) {  // strict: ties keep the lower group
-          best = d2;
-          bg = g;
+          for (int x = 0; x < TPR; ++x) ip += part.ip[(x * BQ + tid) * G + g];
+          // |q - c|^2 in [0, 2^31]: exact in unsigned 32-bit arithmetic
+          const uint32_t d2 = static_cast<uint32_t>(qq[tid]) + static_cast<uint32_t>(cc2[g]) - 2u * static_cast<uint32_t>(ip);
+          if (g == 0 || d2 < best) {  // strict: ties keep the lower group
+            best = d2;
+            myl = g;
+          }
         }
       }
-      lab[tid] = bg;
-      atomicAdd(&cnt[bg], 1);
+      const uint64_t below = (1ull << (tid % 64)) - 1ull;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint64_t m = __ballot(myl == g);
+        if (myl == g) rank = __popcll(m & below);
+        if (tid % 64 == 0) wcnt[tid / 64][g] = __popcll(m);
+      }
     }
-    __syncthreads();  // labels and counts ready
-#pragma unroll 8
-    for (int r = up * RP; r < r1; ++r) atomicAdd(&sums[lab[r]][uj], static_cast<int>(qi[r][uj]));
-    __syncthreads();  // sums ready
+    __syncthreads();  // group counts per wave ready
+    int cnt[G], off[G];  // rows per group and the group's first position in rowlist
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      cnt[g] = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) cnt[g] += wcnt[w][g];
+      off[g] = g == 0 ? 0 : off[g - 1] + cnt[g - 1];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      cnt_s[g] = cnt[g];
+      off_s[g] = off[g];
+    }
+    if (tid < n) {
+      int pos = rank;
+#pragma unroll
+      for (int g = 0; g < G; ++g) pos += g == myl ? off[g] : 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int g = 0; g < G; ++g) pos += (w < tid / 64 && g == myl) ? wcnt[w][g] : 0;
+      rowlist[pos] = tid;
+    }
+    __syncthreads();  // rowlist ready
+    {
+      // fixed-point sums per group over this thread's column and position range
+      const int p0 = up * RP;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int lo = max(p0, off[g]), hi = min(r1, off[g] + cnt[g]);
+        int acc = 0;
+#pragma unroll 4
+        for (int x = lo; x < hi; ++x) acc += qi[rowlist[x]][uj];
+        part.ip[(up * G + g) * D + uj] = acc;
+      }
+    }
+    if (tid < G) cc2[tid] = 0;
+    __syncthreads();  // partial sums ready
     if (tid < D) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int c = cnt[g];
         if (c > 0) {
-          // rounded mean, halves up: floor((2 s + c) / (2 c)) with a floored division
-          const int num = 2 * sums[g][tid] + c, den = 2 * c;
-          int qv = num / den;
-          if (num % den != 0 && num < 0) --qv;
-          ci[g][tid] = static_cast<short>(qv);
+          int sum = 0;
+#pragma unroll
+          for (int x = 0; x < PARTS; ++x) sum += part.ip[(x * G + g) * D + tid];
+          // rounded mean, halves up: floor((2 s + c) / (2 c)). The exact quotient is
+          // k + f / (2c) with f an integer, so (num + 1/2) / (2c) sits at least 1/512
+          // inside [k, k + 1); its fp32 value (|num| < 2^20, one rcp and one multiply)
+          // is within 4e-4 of it, and the floor is exact.
+          const int num = 2 * sum + c;
+          const float y = (static_cast<float>(num) + 0.5f) * __builtin_amdgcn_rcpf(static_cast<float>(2 * c));
+          ci[g][tid] = static_cast<short>(static_cast<int>(floorf(y)));
         }
       }
     }
-    __syncthreads();  // centroids moved
+    centroid_squares();  // each column is read by the thread that wrote it
+    __syncthreads();  // centroids and their squares ready
   }
 
-  // ---- representatives: fp32 means of the original rows of every group
+  // ---- representatives: fp32 means of the original rows of every group, in
+  // rowlist order (fixed), so the result is deterministic
   {
-    float acc[G];
+    const int p0 = up * RP;
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
-#pragma unroll 8
-    for (int r = up * RP; r < r1; ++r) {
-      const float x = Stage<BF16>::get(rows[r][uj]);
-      const int l = lab[r];
-#pragma unroll
-      for (int g = 0; g < G; ++g) acc[g] += l == g ? x : 0.f;
+    for (int g = 0; g < G; ++g) {
+      const int lo = max(p0, off_s[g]), hi = min(r1, off_s[g] + cnt_s[g]);
+      float acc = 0.f;
+#pragma unroll 4
+      for (int x = lo; x < hi; ++x) acc += Stage<BF16>::get(rows[rowlist[x]][uj]);
+      part.fsum[(up * G + g) * D + uj] = acc;
     }
-#pragma unroll
-    for (int g = 0; g < G; ++g) part.fsum[(up * G + g) * D + uj] = acc[g];
   }
   __syncthreads();
   if (tid < D) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int c = cnt[g];
-      float s = 0.f;
+      const int c = cnt_s[g];
+      float sum = 0.f;
 #pragma unroll
-      for (int x = 0; x < PARTS; ++x) s += part.fsum[(x * G + g) * D + tid];
-      cout[g * D + tid] = c > 0 ? s / static_cast<float>(c) : 0.f;
+      for (int x = 0; x < PARTS; ++x) sum += part.fsum[(x * G + g) * D + tid];
+      cout[g * D + tid] = c > 0 ? sum / static_cast<float>(c) : 0.f;
     }
   }
-  if (tid < G) sout[tid] = cnt[tid];
+  if (tid < G) sout[tid] = cnt_s[tid];
 }
 
 }  // namespace

@@ -118,6 +118,7 @@ struct ScoreArgs {
 };
 
 constexpr int SC_WAVES = 8;
+constexpr int SC_CACHE_CHUNKS = 20;  // units up to 640: logits stay in LDS between the passes
 
 // One workgroup per (b, h, group of 32/G query blocks); wave w takes unit
 // chunks w, w + 8, ... (32 units each). MFMA column (lane) n holds
@@ -125,17 +126,20 @@ constexpr int SC_WAVES = 8;
 // and keeps, per lane, the running maximum and n_j-weighted sum of
 // 2^(x - max) with x = l log2(e); the lane halves and the waves combine them.
 // Pass 2 contracts the chunks again (the representatives and key means are
-// small and stay in L2), scales every lane's normalised masses by its weight
+// small and stay in L2) or, when every chunk's logits fit in LDS (up to 640
+// units), reads them back from there; it scales every lane's masses by its weight
 // n_g / n, sums the G lanes of a query block, and writes S once: each wave
 // transposes its block through LDS so that every store instruction covers two
 // contiguous 128-byte row segments of S.
-template <int D, int G>
+template <int D, int G, bool CACHE>
 __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   constexpr int HALF = D / 2;  // lane half h contracts d in [h*HALF, (h+1)*HALF)
   constexpr int QB = 32 / G;   // query blocks per workgroup
   __shared__ float red_m[SC_WAVES][32];
   __shared__ float red_s[SC_WAVES][32];
   __shared__ float tile[SC_WAVES][QB][33];  // one chunk of one wave: [query block][unit], padded
+  // CACHE: pass 1 keeps every chunk's logits (each lane its own 16) for pass 2
+  __shared__ float lcache[CACHE ? SC_CACHE_CHUNKS * 16 * 64 : 1];
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int n = lane % 32, h = lane / 32;
@@ -198,6 +202,10 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   float run_m = -INFINITY, run_s = 0.f;
   for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
     const f32x16 acc = logits(ch);
+    if constexpr (CACHE) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lcache[(ch * 16 + r) * 64 + lane] = acc[r];
+    }
     float lmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) lmax = fmaxf(lmax, acc[r]);
@@ -243,7 +251,13 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   const float scale = invZ * wgt;
   float* sbase = a.S + (static_cast<size_t>(bh) * a.nQB + qg * QB) * a.nKU;
   for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
-    const f32x16 acc = logits(ch);
+    f32x16 acc;
+    if constexpr (CACHE) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = lcache[(ch * 16 + r) * 64 + lane];  // written by this lane
+    } else {
+      acc = logits(ch);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jl = 8 * (r / 4) + 4 * h + (r % 4);
@@ -317,7 +331,10 @@ hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, cons
   a.n_qgroups = (g.nQB + per_wg - 1) / per_wg;
   a.sm_scale = g.sm_scale;
   const dim3 grid(g.B * g.H * a.n_qgroups), block(64 * SC_WAVES);
-#define BSA_SCORES(D, G) hipLaunchKernelGGL((scores_kernel<D, G>), grid, block, 0, s, a)
+  const bool cache = (g.nKU + 31) / 32 <= SC_CACHE_CHUNKS;
+#define BSA_SCORES(D, G)                                                                  \
+  if (cache) hipLaunchKernelGGL((scores_kernel<D, G, true>), grid, block, 0, s, a);       \
+  else hipLaunchKernelGGL((scores_kernel<D, G, false>), grid, block, 0, s, a)
 #define BSA_SCORES_G(D)                      \
   switch (groups) {                          \
     case 1: BSA_SCORES(D, 1); break;         \
