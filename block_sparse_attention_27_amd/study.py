@@ -12,6 +12,8 @@ with no trained weights: for each logit temperature of a workload it runs
     unweighted   exact k + systematic sample of m, w = 1 for every entry
     weighted     exact k + systematic sample of m, w = 1/pi   (the method)
     sample_only  no exact set, a weighted sample of k+m units
+    *_ibcs       truncation and weighted again, with the scores of the
+                 intra-block clustering scorer (4 groups, 3 iterations)
 
 through ``bsa_attend`` (fp32 output) and reports, against
 ``bsa_attend_dense`` over the valid rows:
@@ -103,11 +105,15 @@ def run_temperature(w, seeds, log=print):
            "m_sample": w.m_sample, "density": round(w.density, 4), "top_mass": round(top_mass, 4),
            "seeds": len(seeds)}
 
+    S_ib = bsa.score_ibcs(base, q, k, perm, groups=4, iters=3)[0]
+
     p_tr = bsa.problem_for(w, out_fp32=1, k_exact=L, m_sample=0)
     idx, wt = bsa.select(p_tr, S)
     res["truncation"], res["truncation_dr"] = err(p_tr, idx, wt)
+    idx, wt = bsa.select(p_tr, S_ib)
+    res["truncation_ibcs"], res["truncation_ibcs_dr"] = err(p_tr, idx, wt)
 
-    runs = {"unweighted": [], "weighted": [], "sample_only": []}
+    runs = {"unweighted": [], "weighted": [], "sample_only": [], "weighted_ibcs": []}
     for s in seeds:
         p = bsa.problem_for(w, seed=s, out_fp32=1)
         idx, wt = bsa.select(p, S)
@@ -116,6 +122,8 @@ def run_temperature(w, seeds, log=print):
         p0 = bsa.problem_for(w, seed=s, out_fp32=1, k_exact=0, m_sample=L)
         idx0, wt0 = bsa.select(p0, S)
         runs["sample_only"].append(err(p0, idx0, wt0))
+        idx, wt = bsa.select(p, S_ib)
+        runs["weighted_ibcs"].append(err(p, idx, wt))
     for name, vals in runs.items():
         errs = [e for e, _ in vals]
         res[name] = statistics.mean(errs)
