@@ -34,6 +34,8 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
   __shared__ int s_base[DENSE ? 1 : LMAX];
   __shared__ int s_lim[DENSE ? 1 : LMAX];
   __shared__ float s_lw[DENSE ? 1 : LMAX];
+  // permuted sequences: gathered key rows of tiles t+1 .. t+3, slot (t & 3)
+  __shared__ int s_grow[PERM ? 4 * TILE : 1];
 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
@@ -103,6 +105,12 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
     stage_one<D, NW, BK, PERM, false>(a, kb, K0, meta0, swave, lane, k_lane_off);
     stage_one<D, NW, BK, PERM, true>(a, vb, V0, meta0, swave, lane, v_lane_off);
     if (n_tiles > 1) stage_one<D, NW, BK, PERM, false>(a, kb, K1, meta1, swave, lane, k_lane_off);
+    if constexpr (PERM) {  // gathered rows of tiles 1 and 2 for the first step's staging
+      if (tid < TILE) {
+        s_grow[1 * TILE + tid] = tile_row_gather<BK>(a, meta1, tid);
+        s_grow[2 * TILE + tid] = tile_row_gather<BK>(a, meta_of(2), tid);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Running-max bookkeeping. When a tile's scores are complete, its maximum
@@ -154,13 +162,25 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) kf[i] = kread(i);
       const TileMeta mt2 = meta_of(t + 2);
-      // Staging of K(t+2) and V(t+1). With a permutation (a gather per row)
-      // all of it happens here; otherwise one load per few MFMA groups below,
-      // branch-free: past the end of the list the loads fill the free slots
-      // with row 0 of the head, which nothing reads.
+      // Staging of K(t+2) and V(t+1). With a permutation all of it happens
+      // here, from the gathered rows the step before last looked up, and this
+      // step looks up tile t+3's rows (stored at its end); otherwise one load
+      // per few MFMA groups below, branch-free: past the end of the list the
+      // loads fill the free slots with row 0 of the head, which nothing reads.
+      int grow_next = 0;
       if constexpr (PERM) {
-        if (t + 2 < n_tiles) stage_one<D, NW, BK, PERM, false>(a, kb, k_write, mt2, swave, lane, k_lane_off);
-        if (t + 1 < n_tiles) stage_one<D, NW, BK, PERM, true>(a, vb, v_write, mt1, swave, lane, v_lane_off);
+        constexpr int PW_ = StageGeom<D, NW>::PER_WAVE;
+        if (t + 2 < n_tiles) {
+#pragma unroll
+          for (int i = 0; i < PW_; ++i)
+            stage_gathered<D, NW>(kb, k_write, s_grow + ((t + 2) & 3) * TILE, swave, st_r0, k_chunk, i);
+        }
+        if (t + 1 < n_tiles) {
+#pragma unroll
+          for (int i = 0; i < PW_; ++i)
+            stage_gathered<D, NW>(vb, v_write, s_grow + ((t + 1) & 3) * TILE, swave, st_r0, v_chunk, i);
+        }
+        if (tid < TILE && t + 3 < n_tiles) grow_next = tile_row_gather<BK>(a, meta_of(t + 3), tid);
       }
       constexpr int PW = StageGeom<D, NW>::PER_WAVE;
       // staging load k (K loads 0..PW-1, then V) goes with MFMA group 1 + k (NQ + NP) / (2 PW)
@@ -249,6 +269,11 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
           decide(mx);
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (PERM) {
+        // tile t+3's slot held tile t-1, whose last reader (the staging of
+        // V(t-1)) ran two steps ago; readers of the new rows come after a barrier
+        if (tid < TILE) s_grow[((t + 3) & 3) * TILE + tid] = grow_next;
       }
       return mt2;
     };

@@ -211,6 +211,30 @@ __device__ __forceinline__ void stage_ins(const uint16_t* src, BSA_LDS char* dst
                                    (BSA_LDS void*)(dst + (i * NW + swave) * 1024), 16, 0, 0);
 }
 
+// Gathered key row of tile row r for a permuted sequence: unit r / BK, key
+// r % BK -> perm[base + r % BK]; a row past the unit's valid keys, or a gather
+// entry outside [0, N_pad), gives row 0 of the head (its logits are masked).
+template <int BK>
+__device__ __forceinline__ int tile_row_gather(const AttendArgs& a, const TileMeta& m, int r) {
+  const int u = r / BK, o = r % BK;
+  if (o >= pick4(m.lim, u)) return 0;
+  const int g = a.perm[pick4(m.base, u) + o];
+  return static_cast<unsigned>(g) < static_cast<unsigned>(a.N_pad) ? g : 0;
+}
+
+// Instruction i of a tile's staging for a permuted sequence: the tile's
+// gathered rows come from an LDS table (rows[r] for tile row r), so the
+// address is the lane's gathered row plus its fixed chunk byte.
+template <int D, int NW>
+__device__ __forceinline__ void stage_gathered(const uint16_t* src, BSA_LDS char* dst, const int* rows, int swave,
+                                               int r0, uint32_t chunk_off, int i) {
+  using SG = StageGeom<D, NW>;
+  const int gr = rows[i * SG::G + r0];
+  const char* sp = reinterpret_cast<const char*>(src) + static_cast<size_t>(gr) * (2 * D) + chunk_off;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(sp),
+                                   (BSA_LDS void*)(dst + (i * NW + swave) * 1024), 16, 0, 0);
+}
+
 // Rank-sorts the list chunk [c0, c0 + n) of one query block by unit index
 // (ties by position) into the LDS tables; entries with an index outside
 // [0, nKU) or a weight that is not a finite positive number become empty.
