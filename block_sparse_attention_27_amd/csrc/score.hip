@@ -12,10 +12,12 @@
 //
 // block_means_kernel streams Q and K once from HBM (16-byte loads, fp32
 // accumulation, one LDS reduction per block). scores_kernel contracts the
-// fp32 means with v_mfma_f32_32x32x2_f32 in the S^T orientation (a lane holds
-// one query block, its registers 16 units), so each lane keeps its own
-// running max and n_j-weighted sum; a second pass recomputes the logits and
-// writes S once, normalised.
+// fp32 means in the S^T orientation (a lane holds one query block, its
+// registers 16 units) on bf16 MFMAs with every value split into bf16 hi + lo
+// parts (three products, fp32 accumulation: about 1e-5 relative), so each
+// lane keeps its own running max and n_j-weighted sum; a second pass
+// recomputes the logits (or reads them back from LDS) and writes S once,
+// normalised.
 #include "bsa_internal.hpp"
 
 #include <math.h>
@@ -108,6 +110,20 @@ __global__ __launch_bounds__(MEAN_THREADS) void block_means_kernel(MeansArgs a) 
   }
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// x (8 floats) = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both round
+// to nearest even: |x - hi - lo| <= 2^-18 |x|.
+__device__ __forceinline__ void split_bf16(f32x4 x0, f32x4 x1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int z = 0; z < 8; ++z) {
+    const float x = z < 4 ? x0[z] : x1[z - 4];
+    const __bf16 h = static_cast<__bf16>(x);
+    hi[z] = h;
+    lo[z] = static_cast<__bf16>(x - static_cast<float>(h));
+  }
+}
+
 struct ScoreArgs {
   const float* q_rep;     // [bh][nQB][G][D] query representatives (block means when G = 1)
   const int32_t* q_size;  // [bh][nQB][G] rows per representative; nullptr: weight 1 (G = 1)
@@ -133,7 +149,6 @@ constexpr int SC_CACHE_CHUNKS = 20;  // units up to 640: logits stay in LDS betw
 // contiguous 128-byte row segments of S.
 template <int D, int G, bool CACHE>
 __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
-  constexpr int HALF = D / 2;  // lane half h contracts d in [h*HALF, (h+1)*HALF)
   constexpr int QB = 32 / G;   // query blocks per workgroup
   __shared__ float red_m[SC_WAVES][32];
   __shared__ float red_s[SC_WAVES][32];
@@ -148,13 +163,15 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   const int qb = qg * QB + ib;  // query block of this lane
   const bool qok = qb < a.nQB;
   const size_t rep = (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * G;
-  const float* qm = a.q_rep + (rep + grp) * D + h * HALF;
-  float qv[HALF];
+  // B operand, step s of 16 dimensions: lane half h supplies dimensions
+  // 16 s + 8 h .. +7, each split into bf16 hi + lo parts
+  const float* qm = a.q_rep + (rep + grp) * D + 8 * h;
+  bf16x8 qhi[D / 16], qlo[D / 16];
 #pragma unroll
-  for (int z = 0; z < HALF / 4; ++z) {
-    const f32x4 x = qok ? *reinterpret_cast<const f32x4*>(qm + 4 * z) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int y = 0; y < 4; ++y) qv[4 * z + y] = x[y];
+  for (int st = 0; st < D / 16; ++st) {
+    const f32x4 x0 = qok ? *reinterpret_cast<const f32x4*>(qm + 16 * st) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 x1 = qok ? *reinterpret_cast<const f32x4*>(qm + 16 * st + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    split_bf16(x0, x1, qhi[st], qlo[st]);
   }
   // weight n_g / n of this lane's representative; a block with no valid row
   // scores with its first (zero) representative alone
@@ -169,30 +186,36 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     }
     wgt = tot > 0 ? static_cast<float>(mine) / static_cast<float>(tot) : (grp == 0 ? 1.f : 0.f);
   }
-  const float* kmb = a.k_mean + static_cast<size_t>(bh) * a.nKU * D + h * HALF;
+  const float* kmb = a.k_mean + static_cast<size_t>(bh) * a.nKU * D + 8 * h;
   const int n_chunks = (a.nKU + 31) / 32;
   const float c2 = a.sm_scale * 1.4426950408889634f;  // logits in log2 units
 
   // x for the 32 units of chunk ch: register r holds unit j0 + 8 (r/4) + 4 h + r%4;
-  // -inf for units with no valid key
+  // -inf for units with no valid key. <k, q> = kh.qh + kh.ql + kl.qh on bf16
+  // MFMAs (fp32 accumulation): each value is hi + lo to 2^-18 relative and the
+  // dropped kl.ql term is below 2^-18 of the product.
   auto logits = [&](int ch) {
     const int j0 = ch * 32;
     const int ja = j0 + n;  // A-operand row (unit) of this lane
     const bool aok = ja < a.nKU;
-    f32x16 acc = f32x16{};
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
     const float* km = kmb + static_cast<size_t>(aok ? ja : 0) * D;
 #pragma unroll
-    for (int z = 0; z < HALF / 4; ++z) {
-      const f32x4 kv = aok ? *reinterpret_cast<const f32x4*>(km + 4 * z) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int y = 0; y < 4; ++y)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[y], qv[4 * z + y], acc, 0, 0, 0);
+    for (int st = 0; st < D / 16; ++st) {
+      const f32x4 x0 = aok ? *reinterpret_cast<const f32x4*>(km + 16 * st) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 x1 = aok ? *reinterpret_cast<const f32x4*>(km + 16 * st + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 khi, klo;
+      split_bf16(x0, x1, khi, klo);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qhi[st], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qlo[st], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qhi[st], acc0, 0, 0, 0);
     }
+    f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = j0 + 8 * (r / 4) + 4 * h + (r % 4);
       const bool valid = j < a.nKU && j * a.block_k < a.N;
-      acc[r] = valid ? acc[r] * c2 : -INFINITY;
+      acc[r] = valid ? (acc0[r] + acc1[r]) * c2 : -INFINITY;
     }
     return acc;
   };
