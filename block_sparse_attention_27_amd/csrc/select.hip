@@ -157,6 +157,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   __shared__ uint32_t sbits[SEL_THREADS * E];
   __shared__ uint64_t red64[SEL_WAVES];
   __shared__ uint32_t red32[SEL_WAVES];
+  __shared__ uint32_t cnt2[2][SEL_WAVES];  // per-wave counts, alternating buffers
 
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -182,13 +183,22 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
 
   // ---- 1. exact set: T = k-th largest key, ties by lower index ----
   if (a.k > 0) {
+    // counts from ballots (cand >= 1 and invalid units hold key 0); one
+    // barrier per bit: a buffer is rewritten two bits later, after every
+    // thread has passed the barrier that follows its reads
+    const int wave = tid / 64;
     uint32_t T = 0;
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
       uint32_t c = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) c += (valid[e] && key[e] >= cand) ? 1u : 0u;
-      if (block_sum(c, red32) >= static_cast<uint32_t>(a.k)) T = cand;
+      for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
+      if (tid % 64 == 0) cnt2[bit & 1][wave] = c;
+      __syncthreads();
+      uint32_t tot = 0;
+#pragma unroll
+      for (int x = 0; x < SEL_WAVES; ++x) tot += cnt2[bit & 1][x];
+      if (tot >= static_cast<uint32_t>(a.k)) T = cand;
     }
     uint32_t gt = 0, eq = 0;
 #pragma unroll
@@ -258,7 +268,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
     }
 
     // ---- 2c. fixed-point pi ----
+    // (m - t) q_j < 2^33 and Q_U < 2^33 are exact in fp64, and so is their
+    // product form below; an uncapped unit has (m - t) q_j < Q_U, so its
+    // correctly rounded ratio is below 1 and 2^32 ratio fits 32 bits.
     const uint64_t mt = static_cast<uint64_t>(a.m) - t;
+    const double mt_d = static_cast<double>(static_cast<uint32_t>(mt));
+    const double qu_d = static_cast<double>(QU);
     uint64_t usum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -266,8 +281,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
       if (capped[e]) {
         pi[e] = 1ull << 32;
       } else {
-        const double ratio = static_cast<double>(mt * q[e]) / static_cast<double>(QU);
-        pi[e] = static_cast<uint64_t>(ratio * 4294967296.0);
+        const double ratio = (mt_d * static_cast<double>(q[e])) / qu_d;
+        pi[e] = static_cast<uint32_t>(ratio * 4294967296.0);
         usum += pi[e];
       }
     }
@@ -309,6 +324,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
     const uint64_t u = philox_word0(static_cast<uint32_t>(i), static_cast<uint32_t>(hd),
                                     static_cast<uint32_t>(b), 0u, a.seed_lo, a.seed_hi);
     auto below = [u](uint64_t x) -> uint64_t { return x > u ? ((x - u - 1) >> 32) + 1 : 0; };
+    // every key is in registers and the exscan's barriers have passed: the
+    // staging array hands pi - 1 of each sampled slot (1 <= pi <= 2^32) to the
+    // thread that writes its weight (k + m <= nV slots)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (!inR[e]) continue;
@@ -316,11 +334,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
       c += pi[e];
       const uint64_t n0 = below(c0), n1 = below(c);
       if (n1 > n0 && n0 < static_cast<uint64_t>(a.m)) {  // n0 < m always holds when sum pi = m 2^32
-        const int slot = a.k + static_cast<int>(n0);
-        irow[slot] = tid * E + e;
-        wrow[slot] = static_cast<float>(4294967296.0 / static_cast<double>(pi[e]));
+        irow[a.k + static_cast<int>(n0)] = tid * E + e;
+        sbits[n0] = static_cast<uint32_t>(pi[e] - 1);
       }
     }
+    __syncthreads();
+    for (int x = tid; x < a.m; x += SEL_THREADS)
+      wrow[a.k + x] = static_cast<float>(4294967296.0 / (static_cast<double>(sbits[x]) + 1.0));
   }
 }
 
