@@ -25,7 +25,7 @@
 // the mixture, by n_g / n, of every group's n_j-weighted softmax over the key
 // units.
 //
-// One workgroup (256 threads) per (b, h, query block). The block's rows are
+// One workgroup (512 threads) per (b, h, query block). The block's rows are
 // staged once in LDS in their input type, next to their 16-bit fixed-point
 // copies. A distance is |q|^2 + |c|^2 - 2 <q, c> with the inner product on
 // v_dot2_i32_i16 (two dimensions per instruction, exact); TPR threads share a
@@ -41,7 +41,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int CL_THREADS = 256;
+constexpr int CL_THREADS = 512;
 
 struct ClusterArgs {
   const void* q;
@@ -162,17 +162,29 @@ __global__ __launch_bounds__(CL_THREADS) void block_clusters_kernel(ClusterArgs 
   if (mx > 0.f) frexpf(mx, &ex);
   const int sh = mx > 0.f ? FIXED_BITS - ex : 0;
 
-  // ---- fixed-point copies (|q_int| <= 2^11) from the staged registers
+  // ---- fixed-point copies (|q_int| <= 2^11) from the staged registers.
+  // x 2^sh is exact, and adding 1.5 2^23 rounds it to the nearest integer
+  // (ties to even) in the last place of a float in [2^23, 2^24), whose bits
+  // minus those of 1.5 2^23 are that integer.
+  constexpr float MAGIC = 12582912.f;  // 1.5 2^23
 #pragma unroll
   for (int pp = 0; pp < MAXP; ++pp) {
     const int r = rg + pp * RPP;
     if (r < n) {
       const T* xv = reinterpret_cast<const T*>(&xr[pp]);
-      short v[EPC];
+      uint32_t w[EPC / 2];
 #pragma unroll
-      for (int z = 0; z < EPC; ++z) v[z] = static_cast<short>(__float2int_rn(ldexpf(Stage<BF16>::get(xv[z]), sh)));
+      for (int z = 0; z < EPC / 2; ++z) {
+        const uint32_t i0 = __float_as_uint(ldexpf(Stage<BF16>::get(xv[2 * z]), sh) + MAGIC) - 0x4B400000u;
+        const uint32_t i1 = __float_as_uint(ldexpf(Stage<BF16>::get(xv[2 * z + 1]), sh) + MAGIC) - 0x4B400000u;
+        w[z] = (i0 & 0xFFFFu) | (i1 << 16);
+      }
+      if constexpr (EPC == 8) {
+        *reinterpret_cast<u32x4*>(&qi[r][cc * EPC]) = u32x4{w[0], w[1], w[2], w[3]};
+      } else {
 #pragma unroll
-      for (int z = 0; z < EPC; ++z) qi[r][cc * EPC + z] = v[z];
+        for (int z = 0; z < EPC / 2; ++z) *reinterpret_cast<uint32_t*>(&qi[r][cc * EPC + 2 * z]) = w[z];
+      }
     }
   }
   __syncthreads();  // rows and fixed-point rows ready
@@ -291,8 +303,9 @@ __global__ __launch_bounds__(CL_THREADS) void block_clusters_kernel(ClusterArgs 
       for (int g = 0; g < G; ++g) {
         const int lo = max(p0, off[g]), hi = min(r1, off[g] + cnt[g]);
         int acc = 0;
+        const short* qcol = &qi[0][0] + uj;
 #pragma unroll 4
-        for (int x = lo; x < hi; ++x) acc += qi[rowlist[x]][uj];
+        for (int x = lo; x < hi; ++x) acc += qcol[__umul24(rowlist[x], LDI)];
         part.ip[(up * G + g) * D + uj] = acc;
       }
     }
@@ -328,8 +341,9 @@ __global__ __launch_bounds__(CL_THREADS) void block_clusters_kernel(ClusterArgs 
     for (int g = 0; g < G; ++g) {
       const int lo = max(p0, off_s[g]), hi = min(r1, off_s[g] + cnt_s[g]);
       float acc = 0.f;
+      const T* rcol = &rows[0][0] + uj;
 #pragma unroll 4
-      for (int x = lo; x < hi; ++x) acc += Stage<BF16>::get(rows[rowlist[x]][uj]);
+      for (int x = lo; x < hi; ++x) acc += Stage<BF16>::get(rcol[__umul24(rowlist[x], LD)]);
       part.fsum[(up * G + g) * D + uj] = acc;
     }
   }
