@@ -15,6 +15,8 @@ Modules, in the order the method runs:
   scoring    block means and the estimated-attention score matrix S
   ibcs       the intra-block clustering scorer: k-means groups per query block,
              S as the size-weighted mixture of the groups' estimated masses
+  stats_score  the statistics-aware scorer: key units scored by the mass of a
+             Gaussian with their mean and per-dimension variance
   selection  exact top-k set, inclusion probabilities, systematic sample, 1/pi weights
   philox     the counter-based generator that supplies one offset per query block
   attention  weighted sparse attention, dense attention, and the two HT sums
@@ -28,6 +30,7 @@ rocRAND's host-callable Philox4x32-10).
 from .philox import philox4x32_10, philox4x32_10_np, block_offset
 from .scoring import apply_perm, unpermute, valid_counts, block_means, score
 from .ibcs import fixed_point, cluster_block, group_mixture, score_ibcs
+from .stats_score import block_variances, score_stats
 from .selection import (sanitize, exact_set, quantise, water_fill, fixed_point_pi,
                         systematic_sample, inverse_weight, select_row, select, F_BITS, FS_BITS)
 from .attention import (attend, attend_block, attend_dense, dense_block, dense_row_max,
@@ -36,7 +39,7 @@ from .attention import (attend, attend_block, attend_dense, dense_block, dense_r
 __all__ = [
     "philox4x32_10", "philox4x32_10_np", "block_offset",
     "apply_perm", "unpermute", "valid_counts", "block_means", "score",
-    "fixed_point", "cluster_block", "group_mixture", "score_ibcs",
+    "fixed_point", "cluster_block", "group_mixture", "score_ibcs", "block_variances", "score_stats",
     "sanitize", "exact_set", "quantise", "water_fill", "fixed_point_pi",
     "systematic_sample", "inverse_weight", "select_row", "select", "F_BITS", "FS_BITS",
     "attend", "attend_block", "attend_dense", "dense_block", "dense_row_max",
