@@ -11,7 +11,8 @@ Prints one JSON line. `value` is milliseconds per layer (lower is better),
 warm: the timed steps run back to back. `cold` times each call on its own
 after 512 MB of writes have evicted the caches; `plan_reuse` times one
 score + select followed by r attend calls that reuse its lists; `ibcs` times
-the intra-block clustering scorer in place of bsa_score.
+the intra-block clustering scorer in place of bsa_score, `stats` the
+statistics-aware scorer.
 `roofline` describes bsa_attend (bf16 MFMA bound), timed with HIP events on
 the stream it runs on; `cpu_baseline` is the fp64 CPU oracle timed on a
 bounded sample of the same workload on this host's cores.
@@ -230,6 +231,19 @@ def main(argv=None):
     t_ibcs = statistics.mean(e[0].elapsed_time(e[1]) for e in ie)
     del qc, qs
 
+    # statistics-aware scorer (key-unit variances) in place of bsa_score
+    kv = torch.empty_like(km)
+    for _ in range(2):
+        bsa.bsa_score_stats(p, q, k, perm, S, qm, km, kv)
+    se = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
+    for e in se:
+        e[0].record(stream)
+        bsa.bsa_score_stats(p, q, k, perm, S, qm, km, kv)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    t_stats = statistics.mean(e[0].elapsed_time(e[1]) for e in se)
+    del kv
+
     # bsa_attend with a bf16 output, same lists
     out16 = torch.empty_like(q)
     be = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
@@ -306,6 +320,8 @@ def main(argv=None):
                  "flush": "512 MB written before every call"},
         "ibcs": {"groups": ib_g, "iters": ib_t, "t_score_ms": round(t_ibcs, 4),
                  "score_select_share": round((t_ibcs + t_select) / (t_ibcs + t_select + t_attend), 4)},
+        "stats": {"t_score_ms": round(t_stats, 4),
+                  "score_select_share": round((t_stats + t_select) / (t_stats + t_select + t_attend), 4)},
         "plan_reuse": {"r": reuse_r, "ms_per_layer": round(t_reuse, 4),
                        "score_select_share": round((t_score + t_select) / reuse_r / t_reuse, 4)},
         "executed_tflops": round(ach, 1),

@@ -9,10 +9,11 @@ Mirrors of the C entry points (same names and argument order, outputs passed
 in by the caller):
     bsa_score(problem, q, k, perm, S, q_mean, k_mean)
     bsa_score_ibcs(problem, groups, iters, q, k, perm, S, q_cent, q_size, k_mean)
+    bsa_score_stats(problem, q, k, perm, S, q_mean, k_mean, k_var)
     bsa_select(problem, S, idx, w)
     bsa_attend(problem, q, k, v, perm, idx, w, out, lse)
     bsa_attend_dense(problem, q, k, v, perm, out, lse)
-Convenience wrappers that allocate their outputs: score, score_ibcs, select, attend,
+Convenience wrappers that allocate their outputs: score, score_ibcs, score_stats, select, attend,
 attend_dense, sparse_attention (the three steps in order), and SamplingPlan,
 which keeps one score + select result for reuse by later attend calls.
 """
@@ -27,8 +28,8 @@ from .inputs import Workload
 
 __all__ = [
     "Problem", "BsaError", "load_library", "library_path", "problem_for", "out_dtype",
-    "bsa_score", "bsa_score_ibcs", "bsa_select", "bsa_attend", "bsa_attend_dense",
-    "score", "score_ibcs", "select", "attend", "attend_dense", "sparse_attention", "SamplingPlan",
+    "bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_attend", "bsa_attend_dense",
+    "score", "score_ibcs", "score_stats", "select", "attend", "attend_dense", "sparse_attention", "SamplingPlan",
     "BSA_OK", "BSA_ERR_INVALID_ARG", "BSA_ERR_UNSUPPORTED", "BSA_ERR_HIP", "BSA_BF16", "BSA_FP32",
 ]
 
@@ -94,6 +95,8 @@ def load_library():
     lib.bsa_score.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_score_ibcs.restype = ctypes.c_int
     lib.bsa_score_ibcs.argtypes = [P, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsa_score_stats.restype = ctypes.c_int
+    lib.bsa_score_stats.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_select.restype = ctypes.c_int
     lib.bsa_select.argtypes = [P, vp, vp, vp, vp]
     lib.bsa_attend.restype = ctypes.c_int
@@ -190,6 +193,21 @@ def bsa_score_ibcs(p: Problem, groups: int, iters: int, q, k, perm, S, q_cent, q
                                                            _ptr(k_mean), _stream(stream)))
 
 
+def bsa_score_stats(p: Problem, q, k, perm, S, q_mean, k_mean, k_var, stream=None):
+    import torch
+    et = _elem_dtype(p)
+    _expect("q", q, (p.B, p.H, p.N_pad, p.d), et)
+    _expect("k", k, (p.B, p.H, p.N_pad, p.d), et)
+    _expect("perm", perm, (p.N_pad,), torch.int32)
+    _expect("S", S, (p.B, p.H, p.nQB, p.nKU), torch.float32)
+    _expect("q_mean", q_mean, (p.B, p.H, p.nQB, p.d), torch.float32)
+    _expect("k_mean", k_mean, (p.B, p.H, p.nKU, p.d), torch.float32)
+    _expect("k_var", k_var, (p.B, p.H, p.nKU, p.d), torch.float32)
+    _check("bsa_score_stats", load_library().bsa_score_stats(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(perm), _ptr(S),
+                                                             _ptr(q_mean), _ptr(k_mean), _ptr(k_var),
+                                                             _stream(stream)))
+
+
 def bsa_select(p: Problem, S, idx, w, stream=None):
     import torch
     _expect("S", S, (p.B, p.H, p.nQB, p.nKU), torch.float32)
@@ -252,6 +270,18 @@ def score_ibcs(p: Problem, q, k, perm=None, groups: int = 4, iters: int = 3, str
     km = torch.empty((p.B, p.H, p.nKU, p.d), dtype=torch.float32, device=dev)
     bsa_score_ibcs(p, groups, iters, q, k, perm, S, qc, qs, km, stream)
     return S, qc, qs, km
+
+
+def score_stats(p: Problem, q, k, perm=None, stream=None):
+    """Returns (S, q_mean, k_mean, k_var)."""
+    import torch
+    dev = q.device
+    S = torch.empty((p.B, p.H, p.nQB, p.nKU), dtype=torch.float32, device=dev)
+    qm = torch.empty((p.B, p.H, p.nQB, p.d), dtype=torch.float32, device=dev)
+    km = torch.empty((p.B, p.H, p.nKU, p.d), dtype=torch.float32, device=dev)
+    kv = torch.empty((p.B, p.H, p.nKU, p.d), dtype=torch.float32, device=dev)
+    bsa_score_stats(p, q, k, perm, S, qm, km, kv, stream)
+    return S, qm, km, kv
 
 
 def select(p: Problem, S, stream=None):

@@ -95,9 +95,24 @@ bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const i
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(S, 4) || !aligned(q_mean, 16) || !aligned(k_mean, 16))
     return BSA_ERR_INVALID_ARG;
   if (perm && !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
-  st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, false, stream));
+  st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, nullptr, false, stream));
   if (st != BSA_OK) return st;
-  return from_hip(bsa::launch_scores(g, 1, q_mean, nullptr, k_mean, S, stream));
+  return from_hip(bsa::launch_scores(g, 1, q_mean, nullptr, k_mean, nullptr, S, stream));
+}
+
+bsa_status bsa_score_stats(const bsa_problem* p, const void* q, const void* k, const int32_t* perm, float* S,
+                           float* q_mean, float* k_mean, float* k_var, hipStream_t stream) {
+  bsa::Geometry g;
+  bsa_status st = check_problem(p, &g);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !S || !q_mean || !k_mean || !k_var) return BSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(S, 4) || !aligned(q_mean, 16) || !aligned(k_mean, 16) ||
+      !aligned(k_var, 16))
+    return BSA_ERR_INVALID_ARG;
+  if (perm && !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
+  st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, k_var, false, stream));
+  if (st != BSA_OK) return st;
+  return from_hip(bsa::launch_scores(g, 1, q_mean, nullptr, k_mean, k_var, S, stream));
 }
 
 bsa_status bsa_score_ibcs(const bsa_problem* p, int32_t groups, int32_t iters, const void* q, const void* k,
@@ -113,11 +128,11 @@ bsa_status bsa_score_ibcs(const bsa_problem* p, int32_t groups, int32_t iters, c
       !aligned(k_mean, 16))
     return BSA_ERR_INVALID_ARG;
   if (perm && !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
-  st = from_hip(bsa::launch_block_means(g, q, k, perm, nullptr, k_mean, true, stream));
+  st = from_hip(bsa::launch_block_means(g, q, k, perm, nullptr, k_mean, nullptr, true, stream));
   if (st != BSA_OK) return st;
   st = from_hip(bsa::launch_block_clusters(g, groups, iters, q, perm, q_cent, q_size, stream));
   if (st != BSA_OK) return st;
-  return from_hip(bsa::launch_scores(g, groups, q_cent, q_size, k_mean, S, stream));
+  return from_hip(bsa::launch_scores(g, groups, q_cent, q_size, k_mean, nullptr, S, stream));
 }
 
 bsa_status bsa_select(const bsa_problem* p, const float* S, int32_t* idx, float* w, hipStream_t stream) {

@@ -17,13 +17,15 @@ struct Geometry {
 };
 
 // ---- scoring ----
-// keys_only: key-unit means only (q and q_mean unused)
+// keys_only: key-unit means only (q and q_mean unused); k_var != nullptr: also
+// the per-dimension population variance of every key unit
 hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, const int32_t* perm,
-                              float* q_mean, float* k_mean, bool keys_only, hipStream_t s);
+                              float* q_mean, float* k_mean, float* k_var, bool keys_only, hipStream_t s);
 // groups in {1, 2, 4, 8}: q_rep holds `groups` representatives per query block,
-// q_size their row counts (nullptr with groups == 1: weight 1)
+// q_size their row counts (nullptr with groups == 1: weight 1); k_var != nullptr
+// (groups == 1): statistics-aware logits s <q, k> + (s^2/2) <q^2, var>
 hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, const int32_t* q_size,
-                         const float* k_mean, float* S, hipStream_t s);
+                         const float* k_mean, const float* k_var, float* S, hipStream_t s);
 // k-means of every query block's valid rows: `groups` centroids and row counts
 hipError_t launch_block_clusters(const Geometry& g, int groups, int iters, const void* q,
                                  const int32_t* perm, float* q_cent, int32_t* q_size, hipStream_t s);

@@ -37,6 +37,7 @@ struct MeansArgs {
   const int32_t* perm;
   float* q_mean;
   float* k_mean;
+  float* k_var;  // nullptr, or per-dimension population variance of every key unit
   int N, N_pad, block_q, block_k, nQB, nKU, n_bh;
   int first;  // logical block of workgroup 0 (n_bh * nQB: key units only)
 };
@@ -101,12 +102,42 @@ __global__ __launch_bounds__(MEAN_THREADS) void block_means_kernel(MeansArgs a) 
 #pragma unroll
   for (int e = 0; e < EPC; ++e) red[rg][cc * EPC + e] = acc[e];
   __syncthreads();
+  __shared__ float mean_s[D];
   if (tid < D) {
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < RPP; ++r) s += red[r][tid];
     float* out = (is_q ? a.q_mean : a.k_mean) + (static_cast<size_t>(bh) * per + bi) * D;
-    out[tid] = nvalid > 0 ? s / static_cast<float>(nvalid) : 0.f;
+    const float m = nvalid > 0 ? s / static_cast<float>(nvalid) : 0.f;
+    out[tid] = m;
+    mean_s[tid] = m;
+  }
+  if (is_q || a.k_var == nullptr) return;  // whole workgroup
+  // key units: population variance from the deviations of the staged rows
+  __syncthreads();  // means ready; red is free
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    if (rg + p * RPP < nvalid) {
+#pragma unroll
+      for (int z = 0; z < EPC; ++z) {
+        float xv;
+        if constexpr (BF16) xv = (z % 2) ? bf16_hi(x[p][z / 2]) : bf16_lo(x[p][z / 2]);
+        else xv = __uint_as_float(x[p][z]);
+        const float dv = xv - mean_s[cc * EPC + z];
+        acc[z] = fmaf(dv, dv, acc[z]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) red[rg][cc * EPC + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) s += red[r][tid];
+    a.k_var[(static_cast<size_t>(bh) * per + bi) * D + tid] = nvalid > 0 ? s / static_cast<float>(nvalid) : 0.f;
   }
 }
 
@@ -128,6 +159,7 @@ struct ScoreArgs {
   const float* q_rep;     // [bh][nQB][G][D] query representatives (block means when G = 1)
   const int32_t* q_size;  // [bh][nQB][G] rows per representative; nullptr: weight 1 (G = 1)
   const float* k_mean;
+  const float* k_var;     // STATS: per-dimension variance of every key unit
   float* S;
   int N, block_k, nQB, nKU, n_qgroups;
   float sm_scale;
@@ -147,7 +179,7 @@ constexpr int SC_CACHE_CHUNKS = 20;  // units up to 640: logits stay in LDS betw
 // n_g / n, sums the G lanes of a query block, and writes S once: each wave
 // transposes its block through LDS so that every store instruction covers two
 // contiguous 128-byte row segments of S.
-template <int D, int G, bool CACHE>
+template <int D, int G, bool CACHE, bool STATS>
 __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   constexpr int QB = 32 / G;   // query blocks per workgroup
   __shared__ float red_m[SC_WAVES][32];
@@ -166,12 +198,18 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   // B operand, step s of 16 dimensions: lane half h supplies dimensions
   // 16 s + 8 h .. +7, each split into bf16 hi + lo parts
   const float* qm = a.q_rep + (rep + grp) * D + 8 * h;
-  bf16x8 qhi[D / 16], qlo[D / 16];
+  // STATS: steps D/16 .. 2D/16 - 1 carry (s/2) q^2 against the key-unit variances
+  constexpr int NST = (STATS ? 2 : 1) * (D / 16);
+  bf16x8 qhi[NST], qlo[NST];
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
     const f32x4 x0 = qok ? *reinterpret_cast<const f32x4*>(qm + 16 * st) : f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 x1 = qok ? *reinterpret_cast<const f32x4*>(qm + 16 * st + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
     split_bf16(x0, x1, qhi[st], qlo[st]);
+    if constexpr (STATS) {
+      const float hs = 0.5f * a.sm_scale;
+      split_bf16(hs * x0 * x0, hs * x1 * x1, qhi[D / 16 + st], qlo[D / 16 + st]);
+    }
   }
   // weight n_g / n of this lane's representative; a block with no valid row
   // scores with its first (zero) representative alone
@@ -187,6 +225,7 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     wgt = tot > 0 ? static_cast<float>(mine) / static_cast<float>(tot) : (grp == 0 ? 1.f : 0.f);
   }
   const float* kmb = a.k_mean + static_cast<size_t>(bh) * a.nKU * D + 8 * h;
+  const float* kvb = STATS ? a.k_var + static_cast<size_t>(bh) * a.nKU * D + 8 * h : kmb;
   const int n_chunks = (a.nKU + 31) / 32;
   const float c2 = a.sm_scale * 1.4426950408889634f;  // logits in log2 units
 
@@ -199,11 +238,13 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     const int ja = j0 + n;  // A-operand row (unit) of this lane
     const bool aok = ja < a.nKU;
     f32x16 acc0 = f32x16{}, acc1 = f32x16{};
-    const float* km = kmb + static_cast<size_t>(aok ? ja : 0) * D;
+    const size_t koff_ = static_cast<size_t>(aok ? ja : 0) * D;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const f32x4 x0 = aok ? *reinterpret_cast<const f32x4*>(km + 16 * st) : f32x4{0.f, 0.f, 0.f, 0.f};
-      const f32x4 x1 = aok ? *reinterpret_cast<const f32x4*>(km + 16 * st + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < NST; ++st) {
+      // steps past D/16 read the unit's variances (STATS)
+      const float* km = (st < D / 16 ? kmb : kvb) + koff_ + 16 * (st % (D / 16));
+      const f32x4 x0 = aok ? *reinterpret_cast<const f32x4*>(km) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const f32x4 x1 = aok ? *reinterpret_cast<const f32x4*>(km + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
       bf16x8 khi, klo;
       split_bf16(x0, x1, khi, klo);
       acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qhi[st], acc0, 0, 0, 0);
@@ -310,13 +351,14 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
 }  // namespace
 
 hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, const int32_t* perm,
-                              float* q_mean, float* k_mean, bool keys_only, hipStream_t s) {
+                              float* q_mean, float* k_mean, float* k_var, bool keys_only, hipStream_t s) {
   MeansArgs a;
   a.q = q;
   a.k = k;
   a.perm = perm;
   a.q_mean = q_mean;
   a.k_mean = k_mean;
+  a.k_var = k_var;
   a.N = g.N;
   a.N_pad = g.N_pad;
   a.block_q = g.block_q;
@@ -340,11 +382,12 @@ hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, c
 }
 
 hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, const int32_t* q_size,
-                         const float* k_mean, float* S, hipStream_t s) {
+                         const float* k_mean, const float* k_var, float* S, hipStream_t s) {
   ScoreArgs a;
   a.q_rep = q_rep;
   a.q_size = q_size;
   a.k_mean = k_mean;
+  a.k_var = k_var;
   a.S = S;
   a.N = g.N;
   a.block_k = g.block_k;
@@ -355,9 +398,20 @@ hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, cons
   a.sm_scale = g.sm_scale;
   const dim3 grid(g.B * g.H * a.n_qgroups), block(64 * SC_WAVES);
   const bool cache = (g.nKU + 31) / 32 <= SC_CACHE_CHUNKS;
+  if (k_var != nullptr) {  // statistics-aware scoring: one representative per query block
+    if (groups != 1) return hipErrorInvalidValue;
+    if (g.d == 128) {
+      if (cache) hipLaunchKernelGGL((scores_kernel<128, 1, true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((scores_kernel<128, 1, false, true>), grid, block, 0, s, a);
+    } else {
+      if (cache) hipLaunchKernelGGL((scores_kernel<64, 1, true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((scores_kernel<64, 1, false, true>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+  }
 #define BSA_SCORES(D, G)                                                                  \
-  if (cache) hipLaunchKernelGGL((scores_kernel<D, G, true>), grid, block, 0, s, a);       \
-  else hipLaunchKernelGGL((scores_kernel<D, G, false>), grid, block, 0, s, a)
+  if (cache) hipLaunchKernelGGL((scores_kernel<D, G, true, false>), grid, block, 0, s, a); \
+  else hipLaunchKernelGGL((scores_kernel<D, G, false, false>), grid, block, 0, s, a)
 #define BSA_SCORES_G(D)                      \
   switch (groups) {                          \
     case 1: BSA_SCORES(D, 1); break;         \

@@ -14,6 +14,7 @@ with no trained weights: for each logit temperature of a workload it runs
     sample_only  no exact set, a weighted sample of k+m units
     *_ibcs       truncation and weighted again, with the scores of the
                  intra-block clustering scorer (4 groups, 3 iterations)
+    *_stats      the same with the statistics-aware scorer
 
 through ``bsa_attend`` (fp32 output) and reports, against
 ``bsa_attend_dense`` over the valid rows:
@@ -106,14 +107,17 @@ def run_temperature(w, seeds, log=print):
            "seeds": len(seeds)}
 
     S_ib = bsa.score_ibcs(base, q, k, perm, groups=4, iters=3)[0]
+    S_st = bsa.score_stats(base, q, k, perm)[0]
 
     p_tr = bsa.problem_for(w, out_fp32=1, k_exact=L, m_sample=0)
     idx, wt = bsa.select(p_tr, S)
     res["truncation"], res["truncation_dr"] = err(p_tr, idx, wt)
     idx, wt = bsa.select(p_tr, S_ib)
     res["truncation_ibcs"], res["truncation_ibcs_dr"] = err(p_tr, idx, wt)
+    idx, wt = bsa.select(p_tr, S_st)
+    res["truncation_stats"], res["truncation_stats_dr"] = err(p_tr, idx, wt)
 
-    runs = {"unweighted": [], "weighted": [], "sample_only": [], "weighted_ibcs": []}
+    runs = {"unweighted": [], "weighted": [], "sample_only": [], "weighted_ibcs": [], "weighted_stats": []}
     for s in seeds:
         p = bsa.problem_for(w, seed=s, out_fp32=1)
         idx, wt = bsa.select(p, S)
@@ -124,6 +128,8 @@ def run_temperature(w, seeds, log=print):
         runs["sample_only"].append(err(p0, idx0, wt0))
         idx, wt = bsa.select(p, S_ib)
         runs["weighted_ibcs"].append(err(p, idx, wt))
+        idx, wt = bsa.select(p, S_st)
+        runs["weighted_stats"].append(err(p, idx, wt))
     for name, vals in runs.items():
         errs = [e for e, _ in vals]
         res[name] = statistics.mean(errs)

@@ -11,7 +11,8 @@
  * attention pass in which every sampled block is reweighted by the inverse of
  * its inclusion probability in both the softmax numerator and denominator.
  *
- * Pipeline: bsa_score (or bsa_score_ibcs) -> bsa_select -> bsa_attend.
+ * Pipeline: bsa_score (or bsa_score_ibcs, bsa_score_stats) -> bsa_select ->
+ * bsa_attend.
  * bsa_attend_dense is plain dense attention built on the same tiling, for
  * timing and checking.
  *
@@ -54,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 3
+#define BSA_ABI_VERSION 4
 
 typedef enum bsa_status {
   BSA_OK = 0,
@@ -136,6 +137,21 @@ bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const i
 bsa_status bsa_score_ibcs(const bsa_problem* p, int32_t groups, int32_t iters, const void* q, const void* k,
                           const int32_t* perm, float* S, float* q_cent, int32_t* q_size, float* k_mean,
                           hipStream_t stream);
+
+/*
+ * bsa_score_stats -- statistics-aware scoring of the key units. (Veda,
+ * Abstract: tile selection as reconstruction of full attention, with
+ * statistics-aware tile scoring.) Each key unit is scored by the attention
+ * mass its keys would get if they were Gaussian with the unit's per-dimension
+ * mean and variance:
+ *   k_var[b,h,j,:] = population variance of the n_j valid keys of unit j   (fp32, out)
+ *   l_ij = s <q_mean_i, k_mean_j> + (s^2 / 2) <q_mean_i^2, k_var_j>,  s = sm_scale,
+ *   S[b,h,i,j] = n_j exp(l_ij) / sum_{valid j'} n_j' exp(l_ij');  S = 0 for invalid units.
+ * A unit of identical keys scores as in bsa_score. q_mean, k_mean as in
+ * bsa_score; k_var is [B][H][nKU][d] (16-byte aligned).
+ */
+bsa_status bsa_score_stats(const bsa_problem* p, const void* q, const void* k, const int32_t* perm, float* S,
+                           float* q_mean, float* k_mean, float* k_var, hipStream_t stream);
 
 /*
  * bsa_select -- exact set plus fixed-size weighted sample, per (b, h, i).

@@ -32,7 +32,7 @@ def _declared_functions():
 
 def test_header_declares_the_pipeline():
     names = _declared_functions()
-    for n in ("bsa_score", "bsa_score_ibcs", "bsa_select", "bsa_attend", "bsa_attend_dense",
+    for n in ("bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_attend", "bsa_attend_dense",
               "bsa_status_string", "bsa_abi_version"):
         assert n in names
 
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 3
+    assert lib.bsa_abi_version() == 4
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(1) == b"invalid argument"
     assert lib.bsa_status_string(99) == b"unknown status"
@@ -97,6 +97,7 @@ def test_invalid_problem_rejected_by_every_call(lib, bad):
     p = ctypes.byref(_good(**bad))
     assert lib.bsa_score(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_score_ibcs(p, 4, 3, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_score_stats(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_select(p, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_attend(p, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_attend_dense(p, FAKE, FAKE, FAKE, None, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
@@ -107,6 +108,14 @@ def test_ibcs_groups_and_iterations_checked(lib, groups, iters):
     p = ctypes.byref(_good())
     assert lib.bsa_score_ibcs(p, groups, iters, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
                               None) == bsa.BSA_ERR_INVALID_ARG
+
+
+def test_stats_null_and_misaligned_outputs_rejected(lib):
+    p = ctypes.byref(_good())
+    odd = ctypes.c_void_p(0x7F0000000008)
+    for args in ((None, FAKE, FAKE, FAKE), (FAKE, None, FAKE, FAKE), (FAKE, FAKE, None, FAKE),
+                 (FAKE, FAKE, FAKE, None), (FAKE, FAKE, FAKE, odd), (FAKE, odd, FAKE, FAKE)):
+        assert lib.bsa_score_stats(p, FAKE, FAKE, None, *args, None) == bsa.BSA_ERR_INVALID_ARG
 
 
 def test_ibcs_null_and_misaligned_outputs_rejected(lib):

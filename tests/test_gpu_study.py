@@ -25,7 +25,8 @@ def test_study_dense_limit():
     w = _wl(2, 7)
     assert w.list_len == w.n_valid_units
     r = run_temperature(w, [0, 1], log=lambda m: None)
-    for name in ("truncation", "unweighted", "weighted", "sample_only", "truncation_ibcs", "weighted_ibcs"):
+    for name in ("truncation", "unweighted", "weighted", "sample_only", "truncation_ibcs", "weighted_ibcs",
+                 "truncation_stats", "weighted_stats"):
         assert r[name] < 1e-4, (name, r[name])
     assert abs(r["top_mass"] - 1.0) < 1e-5
 
@@ -34,6 +35,7 @@ def test_study_dense_limit():
 def test_study_sparse_finite(tau):
     print_case(f"estimator study, k=1 m=3 tau={tau}")
     r = run_temperature(_wl(1, 3, tau), [0, 1, 2], log=lambda m: None)
-    for name in ("truncation", "unweighted", "weighted", "sample_only", "truncation_ibcs", "weighted_ibcs"):
+    for name in ("truncation", "unweighted", "weighted", "sample_only", "truncation_ibcs", "weighted_ibcs",
+                 "truncation_stats", "weighted_stats"):
         assert math.isfinite(r[name]) and r[name] > 0, (name, r[name])
     assert 0 < r["top_mass"] <= 1 + 1e-6
