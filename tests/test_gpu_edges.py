@@ -206,3 +206,37 @@ def test_determinism_bitwise():
     torch.cuda.synchronize()
     for a, b in zip(r1, r2):
         assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("perm", [False, True])
+def test_lists_longer_than_one_chunk(perm):
+    # 1,100 list entries per query block: the attention kernel takes them in two sorted chunks
+    # of at most 1,024 entries (with a permutation, the gathered-row ring restarts per chunk)
+    print_case(f"lists of 1100 entries (two chunks), permuted={perm}")
+    w = Workload("long", B=1, H=1, grid=(12, 50, 80), d=128, dtype="bf16", block_q=128, block_k=32,
+                 k_exact=100, m_sample=1000, clusters=16, temperature=1.0, permute=perm, seed=9, select_seed=4)
+    assert w.list_len > 1024 and w.n_valid_units > w.list_len
+    g = generate(w)
+    q, k, v = (to_device(g[x]) for x in ("q", "k", "v"))
+    pm = torch.from_numpy(g["perm"]).cuda() if g["perm"] is not None else None
+    p = bsa.problem_for(w, out_fp32=1)
+    S, _, _ = bsa.score(p, q, k, pm)
+    idx, wt = bsa.select(p, S)
+    out, lse = bsa.attend(p, q, k, v, idx, wt, pm, with_lse=True)
+    torch.cuda.synchronize()
+    idx_h, wt_h = idx.cpu().numpy(), wt.cpu().numpy()
+    assert len(np.unique(idx_h[0, 0, 3])) > 1024  # the lists really hold more than one chunk of units
+    blocks = [0, 97, w.n_qblocks - 1]
+    ref = oracle.attend(host_f64(g["q"]), host_f64(g["k"]), host_f64(g["v"]), w.N, w.block_q, w.block_k,
+                        w.sm_scale, idx_h, wt_h, g["perm"], blocks=[(0, 0, i) for i in blocks])
+    got_all, ref_all = [], []
+    for i, (o_ref, l_ref) in zip(blocks, ref):
+        rows = np.arange(i * w.block_q, (i + 1) * w.block_q)
+        orows = np.where(rows < w.N, g["perm"][rows] if perm else rows, rows)
+        got = out[0, 0, torch.from_numpy(orows).cuda()].cpu().numpy().astype(np.float64)
+        gl = lse[0, 0, torch.from_numpy(orows).cuda()].cpu().numpy().astype(np.float64)
+        ok = rows < w.N
+        assert np.max(np.abs(gl[ok] - l_ref[ok])) < 2e-3
+        got_all.append(got[ok]); ref_all.append(o_ref[ok])
+    got_all, ref_all = np.concatenate(got_all), np.concatenate(ref_all)
+    assert rel_l2(got_all, ref_all) < 2e-3 and np.max(np.abs(got_all - ref_all)) < 1e-2
