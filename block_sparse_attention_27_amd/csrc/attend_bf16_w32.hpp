@@ -183,12 +183,13 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
         if (tid < TILE && t + 3 < n_tiles) grow_next = tile_row_gather<BK>(a, meta_of(t + 3), tid);
       }
       constexpr int PW = StageGeom<D, NW>::PER_WAVE;
-      // staging load k (K loads 0..PW-1, then V) goes with MFMA group 1 + k (NQ + NP) / (2 PW)
+      // staging load k (K loads 0..PW-1, then V) goes with MFMA group 1 + k NQ / (2 PW): spread over
+      // the QK groups, so the last loads still have the PV groups to land before the next barrier
       auto stage_k = [&](int grp) {
         if constexpr (!PERM) {
 #pragma unroll
           for (int k = 0; k < 2 * PW; ++k) {
-            if (1 + k * (D / 8 + D / 8) / (2 * PW) != grp) continue;
+            if (1 + k * (D / 8) / (2 * PW) != grp) continue;
             if (k < PW) stage_ins<D, NW, BK>(kb, k_write, mt2, swave, st_r0, k_chunk, k);
             else stage_ins<D, NW, BK>(vb, v_write, mt1, swave, st_r0, v_chunk, k - PW);
           }
