@@ -330,6 +330,7 @@ def main(argv=None):
         "dense_equiv_frac_peak": round(dense_flops / (t_pass * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "dense_kernel_tflops": None if t_dense is None else round(dense_flops / (t_dense * 1e-3) / 1e12, 1),
         "speedup_vs_dense": None if t_dense is None else round(t_dense / t_pass, 3),
+        "speedup_attend_vs_dense": None if t_dense is None else round(t_dense / t_attend, 3),
         "score_hbm_gbs": round(score_bytes / (t_score * 1e-3) / 1e9, 1),
         "select_hbm_gbs": round(select_bytes / (t_select * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "bsa_attend", "bound": "mfma", "achieved": round(ach, 1),
