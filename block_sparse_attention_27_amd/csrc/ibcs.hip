@@ -330,8 +330,9 @@ __global__ __launch_bounds__(CL_THREADS) void block_clusters_kernel(ClusterArgs 
       }
     }
     centroid_squares();  // each column is read by the thread that wrote it
-    __syncthreads();  // centroids and their squares ready
+    // the next iteration's first barrier publishes the centroids and their squares
   }
+  __syncthreads();  // the last update's reads of the partial sums are done
 
   // ---- representatives: fp32 means of the original rows of every group, in
   // rowlist order (fixed), so the result is deterministic
