@@ -26,7 +26,7 @@
 //
 // Layout: thread t owns the E consecutive units [t E, t E + E), so exclusive
 // scans give ranks in unit order directly. Rows of up to 1024 valid units take
-// one wave each (ballot counts, shuffle sums, no barriers); longer rows take a
+// one wave each (ballot counts, DPP sums and scans, no barriers); longer rows take a
 // 256-thread workgroup.
 #include "bsa_internal.hpp"
 
@@ -96,11 +96,58 @@ __device__ __forceinline__ uint32_t quantise(uint32_t x, int e) {
   return q > 0 ? static_cast<uint32_t>(q) : 1u;
 }
 
+// Cross-lane steps on DPP moves, which stay in the VALU (a lane shuffle is an
+// LDS round trip). Rows of the wave are its four 16-lane groups. A lane whose
+// DPP source is outside its row, or whose row is masked off, receives 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, false));
+}
+template <int CTRL, int ROWS = 0xF, typename T>
+__device__ __forceinline__ T dpp(T v) {
+  if constexpr (sizeof(T) == 8) {
+    return (static_cast<uint64_t>(dpp32<CTRL, ROWS>(static_cast<uint32_t>(v >> 32))) << 32) |
+           dpp32<CTRL, ROWS>(static_cast<uint32_t>(v));
+  } else {
+    return static_cast<T>(dpp32<CTRL, ROWS>(static_cast<uint32_t>(v)));
+  }
+}
+template <typename T>
+__device__ __forceinline__ T lane_value(T v, int l) {
+  if constexpr (sizeof(T) == 8) {
+    return (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v >> 32), l))) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), l));
+  } else {
+    return static_cast<T>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+  }
+}
+// Sum over the wave, in every lane: quad swaps, the half-row and row mirrors
+// (every lane then holds its row's sum), then the four rows in scalars.
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return lane_value(v, 0) + lane_value(v, 16) + lane_value(v, 32) + lane_value(v, 48);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp<0xB1>(v));
+  v = max(v, dpp<0x4E>(v));
+  v = max(v, dpp<0x141>(v));
+  v = max(v, dpp<0x140>(v));
+  return max(max(lane_value(v, 0), lane_value(v, 16)), max(lane_value(v, 32), lane_value(v, 48)));
+}
+// Inclusive prefix sum over lanes: shifts by 1, 2, 4, 8 within each row, then
+// the last lane of row 0 (2) is added to row 1 (3), and lane 31 to rows 2, 3.
+__device__ __forceinline__ uint64_t wave_inclusive_scan(uint64_t x) {
+  x += dpp<0x111>(x);       // row_shr:1
+  x += dpp<0x112>(x);       // row_shr:2
+  x += dpp<0x114>(x);       // row_shr:4
+  x += dpp<0x118>(x);       // row_shr:8
+  x += dpp<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
 }
 
 template <typename T>
@@ -118,8 +165,7 @@ __device__ __forceinline__ T block_sum(T v, T* red) {
 
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(v, off)));
+  v = wave_max_u32(v);
   if (lane == 0) red[wave] = v;
   __syncthreads();
   uint32_t t = 0;
@@ -132,12 +178,7 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
 // Exclusive prefix over threads in index order; `total` receives the block sum.
 __device__ __forceinline__ uint64_t block_exscan(uint64_t v, uint64_t* red, uint64_t& total) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  uint64_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint64_t x = wave_inclusive_scan(v);
   if (lane == 63) red[wave] = x;
   __syncthreads();
   uint64_t before = 0, tot = 0;
@@ -346,26 +387,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
 
 // ---- one wave per row (up to 64 E valid units) --------------------------
 // The same computation with every reduction inside one wave: counts from
-// ballots, sums and scans from lane shuffles, no workgroup barriers. Lane t
+// ballots, sums and scans from DPP moves, no workgroup barriers. Lane t
 // owns units [t E, t E + E).
 constexpr int SELW_WAVES = 4;
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(v, off)));
-  return v;
-}
-
 // Exclusive prefix over lanes; `total` receives the wave sum.
 __device__ __forceinline__ uint64_t wave_exscan(uint64_t v, uint64_t& total) {
-  const int lane = threadIdx.x % 64;
-  uint64_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  total = __shfl(x, 63);
+  const uint64_t x = wave_inclusive_scan(v);
+  total = lane_value(x, 63);
   return x - v;
 }
 
