@@ -179,6 +179,19 @@ constexpr int SC_CACHE_CHUNKS = 20;  // units up to 640: logits stay in LDS betw
 // n_g / n, sums the G lanes of a query block, and writes S once: each wave
 // transposes its block through LDS so that every store instruction covers two
 // contiguous 128-byte row segments of S.
+// Sum over each aligned group of G consecutive lanes (G = 1, 2, 4, 8) on DPP
+// moves: the quad swaps [1, 0, 3, 2] and [2, 3, 0, 1] (lane xor 1, xor 2),
+// then the half-row mirror, which pairs the two quads of an 8-lane group
+// once every lane of a quad holds the quad's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  if constexpr (G >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if constexpr (G >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if constexpr (G >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
 template <int D, int G, bool CACHE, bool STATS>
 __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   constexpr int QB = 32 / G;   // query blocks per workgroup
@@ -327,8 +340,7 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
       const int jl = 8 * (r / 4) + 4 * h + (r % 4);
       const float x = acc[r];
       float v = x == -INFINITY ? 0.f : keys_of(ch * 32 + jl) * exp2f(x - Lm) * scale;
-#pragma unroll
-      for (int off = 1; off < G; off <<= 1) v += __shfl_xor(v, off);  // the G lanes of one query block
+      v = group_sum<G>(v);  // the G lanes of one query block
       if (grp == 0) tile[wave][ib][jl] = v;
     }
     // the block is exchanged between the lanes of this wave only
