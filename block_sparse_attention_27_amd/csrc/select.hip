@@ -209,7 +209,17 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   int32_t* irow = a.idx + static_cast<size_t>(row) * L;
   float* wrow = a.w + static_cast<size_t>(row) * L;
 
-  for (int x = tid; x < a.nV; x += SEL_THREADS) sbits[x] = __float_as_uint(srow[x]);
+  {  // every load of the row in flight at once (coalesced), then through LDS to the unit owners
+    uint32_t v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int x = tid + e * SEL_THREADS;
+      v[e] = x < a.nV ? __float_as_uint(srow[x]) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (tid + e * SEL_THREADS < a.nV) sbits[tid + e * SEL_THREADS] = v[e];
+  }
   __syncthreads();
 
   uint32_t key[E];
@@ -412,7 +422,17 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
   float* wrow = a.w + static_cast<size_t>(row) * L;
 
   uint32_t* sb = sbits[wave];
-  for (int x = lane; x < a.nV; x += 64) sb[x] = __float_as_uint(srow[x]);
+  {  // every load of the row in flight at once (coalesced), then through LDS to the unit owners
+    uint32_t v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int x = lane + 64 * e;
+      v[e] = x < a.nV ? __float_as_uint(srow[x]) : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (lane + 64 * e < a.nV) sb[lane + 64 * e] = v[e];
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
