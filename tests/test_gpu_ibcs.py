@@ -130,3 +130,22 @@ def test_ibcs_full_size_sampled_blocks(name, heads, n_blocks):
         ref = oracle.score_ibcs(qh, kh, w.N, w.block_q, w.block_k, w.sm_scale, 4, 3, pm,
                                 blocks=[(0, 0, i) for i in blocks_i])
         _check_blocks([(0, h, i) for i in blocks_i], S, qc, qs, ref, n_rows, n_units)
+
+
+@pytest.mark.parametrize("bq,groups,dtype", [(128, 4, "bf16"), (64, 8, "bf16"), (128, 8, "fp32")])
+def test_ibcs_last_block_with_fewer_rows_than_groups(bq, groups, dtype):
+    # N = 258: the last query block holds 2 valid rows, so initial centroids coincide and some groups stay empty
+    print_case(f"ibcs ragged tail: bq={bq} G={groups} {dtype}")
+    w = Workload("ibcs_tail", B=1, H=3, grid=(2, 3, 43), d=128, dtype=dtype, block_q=bq, block_k=64,
+                 k_exact=1, m_sample=1, clusters=5, temperature=1.0, permute=False, seed=5)
+    p, (q, k, pm), (S, qc, qs, km) = _run(w, groups, 3)
+    S_ref, c_ref, z_ref, kb = oracle.score_ibcs(host_f64(q), host_f64(k), w.N, bq, 64, w.sm_scale, groups, 3, pm)
+    nQB = p.N_pad // bq
+    n_rows = oracle.valid_counts(w.N, p.N_pad, bq)
+    last = (w.N - 1) // bq  # the last block with a valid row
+    assert n_rows[last] == 2
+    blocks = [(0, h, i) for h in range(w.H) for i in range(nQB)]
+    ref = ([S_ref[x] for x in blocks], [c_ref[x] for x in blocks], [z_ref[x] for x in blocks])
+    _check_blocks(blocks, S, qc, qs, ref, n_rows, -(-w.N // 64))
+    tail = qs[0, :, last]
+    assert np.all(tail.sum(-1) == 2) and np.all((tail > 0).sum(-1) <= 2)
