@@ -156,7 +156,8 @@ __global__ __launch_bounds__(CL_THREADS, BF16 ? (G <= 4 ? 6 : 5) : 1) void block
   constexpr int KPW = BQ / 16 / SPL;         // sums: 16-row steps per wave
   constexpr int PARTS = CL_THREADS / D;      // fp32 means: row ranges
   constexpr int RP = BQ / PARTS;             // fp32 means: rows per range
-  constexpr int NPART_A = 2 * BQ * G > SPL * G * D ? 2 * BQ * G : SPL * G * D;
+  constexpr int LP = BQ + 1;                 // inner products: [part][group][row], padded rows
+  constexpr int NPART_A = 2 * G * LP > SPL * G * D ? 2 * G * LP : SPL * G * D;
   constexpr int NPART = (!BF16 && PARTS * G * D > NPART_A) ? PARTS * G * D : NPART_A;
   static_assert(2 * MT <= NWV && KPW >= 1 && SPL * KPW * 16 == BQ && D % 32 == 0 && D <= 128, "tiling");
   static_assert(G <= 8, "one-hot rows of at most 8 groups sit in registers 0..3 of both lane halves");
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(CL_THREADS, BF16 ? (G <= 4 ? 6 : 5) : 1) void block
       }
       if (gok) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part[(pt * BQ + 32 * mt + 8 * (r / 4) + 4 * lh + r % 4) * G + ln] = acc[r];
+        for (int r = 0; r < 16; ++r) part[(pt * G + ln) * LP + 32 * mt + 8 * (r / 4) + 4 * lh + r % 4] = acc[r];
       }
     }
     __syncthreads();  // inner products ready
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(CL_THREADS, BF16 ? (G <= 4 ? 6 : 5) : 1) void block
         int best = 0;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const int ip = 64 * static_cast<int>(part[(BQ + tid) * G + g]) + static_cast<int>(part[tid * G + g]);
+          const int ip = 64 * static_cast<int>(part[(G + g) * LP + tid]) + static_cast<int>(part[g * LP + tid]);
           const int sc = cc2[g] - 2 * ip;
           if (g == 0 || sc < best) {
             best = sc;
