@@ -28,6 +28,8 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int MEAN_THREADS = 256;
 
@@ -360,6 +362,305 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   }
 }
 
+// Word 3 of a gfx9 buffer resource for raw dword accesses (data format 32):
+// with stride 0 a load at an offset past the record count returns zeros and a
+// store there is dropped.
+constexpr int BUFFER_WORD3 = 0x00020000;
+
+constexpr int SS_CT = 4;  // column tiles per workgroup
+constexpr int SS_US = 2;  // unit halves per workgroup
+constexpr int SS_LT = 36; // row stride (floats) of a wave's transposition tile: 16-byte aligned rows
+
+template <int D>
+__device__ __forceinline__ int kmean_swz(int unit) {  // 16-byte chunk swizzle of a bf16 row of D
+  return D == 128 ? (unit & 15) : ((unit >> 1) & 7);
+}
+
+// One step of a reduce-scatter over lane pairs (lane, partner given by the DPP
+// control): of the K values, the lane keeps the upper half when `upper` (the
+// partner the lower half) and adds the partner's copy of the half it keeps.
+template <int CTRL, int K>
+__device__ __forceinline__ void scatter_step(float (&v)[16], bool upper) {
+#pragma unroll
+  for (int i = 0; i < K / 2; ++i) {
+    const float keep = upper ? v[K / 2 + i] : v[i];
+    const float send = upper ? v[i] : v[K / 2 + i];
+    v[i] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xF, 0xF, false));
+  }
+}
+
+// Sums v (16 values, index 4 m + e) over the G consecutive lanes of a group,
+// each lane keeping 16 / G of the sums in v[0 .. 16 / G - 1]:
+//   G = 2: m = 2 grp + i / 4, e = i % 4;  G = 4: m = grp, e = i;
+//   G = 8: m = grp / 2, e = 2 (grp % 2) + i.
+// The partners are lane xor 1 and xor 2 (quad permutations) and, for G = 8,
+// the mirror lane 7 - i of an 8-lane half-row (it lies in the other quad).
+template <int G>
+__device__ __forceinline__ void group_reduce_scatter(float (&v)[16], int grp) {
+  if constexpr (G == 2) {
+    scatter_step<0xB1, 16>(v, grp & 1);
+  } else if constexpr (G == 4) {
+    scatter_step<0x4E, 16>(v, grp & 2);
+    scatter_step<0xB1, 8>(v, grp & 1);
+  } else {
+    static_assert(G == 8, "group size");
+    scatter_step<0x141, 16>(v, grp & 4);
+    scatter_step<0x4E, 8>(v, grp & 2);
+    scatter_step<0xB1, 4>(v, grp & 1);
+  }
+}
+
+// Score matrix for G >= 2 representatives per query block. The eight waves
+// form four column tiles x two unit halves: wave (ct, us) owns MFMA columns
+// (representatives) 32 ct .. 32 ct + 31 of the workgroup's 128 and the unit
+// chunks us, us + 2, ... The four waves of a unit half load each chunk of 32
+// key means together, split it into bf16 hi + lo parts once and keep it in
+// LDS for all four column tiles: one read of the key means per four column
+// tiles, where a wave of scores_kernel reads and splits every chunk itself.
+// Logits are recomputed in pass 2. The key counts n_j enter as a logit offset
+// log2(n_j / block_k), which is 0 for every unit but a ragged last one.
+template <int D, int G>
+__global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs a) {
+  constexpr int CT = SS_CT, US = SS_US;
+  static_assert(CT * US == SC_WAVES && G >= 2, "wave split");
+  constexpr int QBT = 32 / G;       // query blocks per column tile
+  constexpr int QBW = CT * QBT;     // query blocks per workgroup
+  constexpr int PER = 32 * D / 4 / (64 * CT);  // float4 loads per thread and chunk
+  // [buffer][unit half][hi, lo][unit][d], bf16, 16-byte chunks of a row swizzled
+  __shared__ __align__(16) uint16_t kbuf[2][US][2][32 * D];
+  __shared__ float red_m[SC_WAVES][32];
+  __shared__ float red_s[SC_WAVES][32];
+  __shared__ __align__(16) float tile[SC_WAVES][QBT][SS_LT];
+
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: chunk indices and S rows are scalar
+  const int n = lane % 32, h = lane / 32;
+  const int ct = wave % CT, us = wave / CT;
+  // each XCD takes a contiguous range of workgroups: the ones running on an
+  // XCD at a time then sweep the key means of one or two heads, which stay in
+  // that XCD's L2
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / a.n_qgroups, qg = wg % a.n_qgroups;
+  const int ibt = n / G, grp = n % G;          // query block (in the column tile) and group of this lane
+  const int qb0 = qg * QBW + ct * QBT;         // first query block of the column tile
+  const int qb = qb0 + ibt;
+  const bool qok = qb < a.nQB;
+  const size_t rep = (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * G;
+  const float* qm = a.q_rep + (rep + grp) * D + 8 * h;
+  bf16x8 qhi[D / 16], qlo[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    const f32x4 x0 = qok ? *reinterpret_cast<const f32x4*>(qm + 16 * st) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 x1 = qok ? *reinterpret_cast<const f32x4*>(qm + 16 * st + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    split_bf16(x0, x1, qhi[st], qlo[st]);
+  }
+  // weight n_g / n of this lane's representative; a block with no valid row
+  // scores with its first (zero) representative alone
+  float wgt = 1.f;
+  if (a.q_size != nullptr) {
+    int tot = 0, mine = 0;
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+      const int c = qok ? a.q_size[rep + x] : 0;
+      tot += c;
+      mine = x == grp ? c : mine;
+    }
+    wgt = tot > 0 ? static_cast<float>(mine) / static_cast<float>(tot) : (grp == 0 ? 1.f : 0.f);
+  }
+  // key means of this head through a buffer resource: a load past the last
+  // unit (the ragged chunk, or the chunk after the last) reads zeros
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a.k_mean + static_cast<size_t>(bh) * a.nKU * D), 0, a.nKU * D * 4, BUFFER_WORD3);
+  const int n_chunks = (a.nKU + 31) / 32;
+  const int n_iter = (n_chunks + US - 1) / US;  // the same count for every wave: the barriers match
+  const float c2 = a.sm_scale * 1.4426950408889634f;
+  // units 0 .. nV - 1 hold keys, all block_k of them but the last
+  const int nV = min(a.nKU, (a.N + a.block_k - 1) / a.block_k);
+  const int ch_edge = nV > 0 ? (nV - 1) / 32 : 0;  // chunks from here on hold the last valid unit or none
+  const float tail = nV > 0 ? log2f(static_cast<float>(a.N - (nV - 1) * a.block_k) / static_cast<float>(a.block_k)) : 0.f;
+
+  // staging: thread t = 64 ct + lane of unit half us takes float4 number
+  // t + 64 CT p (p < PER) of the chunk's 32 x D key-mean floats
+  const int gt = 64 * ct + lane;
+  f32x4 xk[PER];
+  auto load_chunk = [&](int ch) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const uint32_t off = static_cast<uint32_t>(ch * 32 * D + 4 * (gt + 64 * CT * p)) * 4u;
+      xk[p] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = gt + 64 * CT * p, unit = idx / (D / 4), d4 = idx % (D / 4);
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const float x0 = xk[p][2 * z], x1 = xk[p][2 * z + 1];
+        const __bf16 h0 = static_cast<__bf16>(x0), h1 = static_cast<__bf16>(x1);
+        const __bf16 l0 = static_cast<__bf16>(x0 - static_cast<float>(h0));
+        const __bf16 l1 = static_cast<__bf16>(x1 - static_cast<float>(h1));
+        hi[z] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+        lo[z] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l0)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l1)) << 16);
+      }
+      // element 4 d4 of the row: 16-byte chunk d4 / 2 (swizzled), 8-byte half d4 % 2
+      const int off = unit * D + 8 * ((d4 / 2) ^ kmean_swz<D>(unit)) + 4 * (d4 % 2);
+      *reinterpret_cast<u32x2*>(&kbuf[buf][us][0][off]) = u32x2{hi[0], hi[1]};
+      *reinterpret_cast<u32x2*>(&kbuf[buf][us][1][off]) = u32x2{lo[0], lo[1]};
+    }
+  };
+  // x for the 32 units of chunk ch (register r: unit ch 32 + 8 (r/4) + 4 h + r%4)
+  // in log2 units, with the key-count offset; -inf for units with no valid key.
+  // The A operand is row n of the staged chunk; every fragment is read before
+  // the first product.
+  auto logits = [&](int ch, int buf) {
+    const uint16_t* kh = &kbuf[buf][us][0][n * D];
+    const uint16_t* kl = &kbuf[buf][us][1][n * D];
+    const int sw = kmean_swz<D>(n);
+    bf16x8 khi[D / 16], klo[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const int c = (2 * st + h) ^ sw;
+      khi[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kh + 8 * c));
+      klo[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + 8 * c));
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[st], qhi[st], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[st], qlo[st], acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo[st], qhi[st], acc0, 0, 0, 0);
+    }
+    f32x16 acc = (acc0 + acc1) * c2;
+    if (ch >= ch_edge) {  // uniform: the chunk of the last valid unit and any after it
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = ch * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+        acc[r] = j < nV - 1 ? acc[r] : (j == nV - 1 ? acc[r] + tail : -INFINITY);
+      }
+    }
+    return acc;
+  };
+
+  // one pass over this unit half's chunks. The chunk of iteration it sits in
+  // buffer it & 1: a buffer is rewritten two iterations later, after the
+  // barrier that follows its reads. A chunk past the last (the second unit
+  // half's final iteration when the chunk count is odd, and the load after
+  // every half's last chunk) reads zeros; its units all get -inf logits, so
+  // body(ch, acc) adds nothing and stores nothing for it. Loads and bodies
+  // are unconditional, so that the wait for a chunk's loads leaves the stores
+  // of S issued after them in flight.
+  auto sweep = [&](auto&& body, auto&& after_first_load) {
+    load_chunk(us);
+    after_first_load();
+    for (int it = 0; it < n_iter; ++it) {
+      const int ch = us + it * US;
+      store_chunk(it & 1);
+      load_chunk(ch + US);
+      __syncthreads();
+      body(ch, logits(ch, it & 1));
+    }
+    __syncthreads();  // the last buffers are read before the next sweep rewrites them
+  };
+
+  // ---- pass 1: running maximum and sum per representative
+  float run_m = -INFINITY, run_s = 0.f;
+  sweep([&](int, const f32x16& acc) {
+    float lmax = acc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) lmax = fmaxf(lmax, acc[r]);
+    // a chunk with no valid unit leaves the state as it is; otherwise nm is
+    // finite and exp2(-inf - nm) = 0 drops the invalid units
+    if (lmax != -INFINITY) {
+      const float nm = fmaxf(run_m, lmax);
+      float sv = run_s * __builtin_amdgcn_exp2f(run_m - nm);  // run_s = 0 while run_m = -inf
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv += __builtin_amdgcn_exp2f(acc[r] - nm);
+      run_s = sv;
+      run_m = nm;
+    }
+  }, [] {});
+  {  // the two lane halves, then the unit halves of the column tile
+    const float om = __shfl_xor(run_m, 32), os = __shfl_xor(run_s, 32);
+    const float nm = fmaxf(run_m, om);
+    float sv = 0.f;
+    if (nm != -INFINITY) sv = run_s * __builtin_amdgcn_exp2f(run_m - nm) + os * __builtin_amdgcn_exp2f(om - nm);
+    run_m = nm;
+    run_s = sv;
+  }
+  if (h == 0) {
+    red_m[wave][n] = run_m;
+    red_s[wave][n] = run_s;
+  }
+  __syncthreads();
+  float Lm = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < US; ++x) Lm = fmaxf(Lm, red_m[x * CT + ct][n]);
+  float Z = 0.f;
+  if (Lm != -INFINITY) {
+#pragma unroll
+    for (int x = 0; x < US; ++x) Z += red_s[x * CT + ct][n] * __builtin_amdgcn_exp2f(red_m[x * CT + ct][n] - Lm);
+  }
+  const float invZ = Z > 0.f ? 1.f / Z : 0.f;
+
+  // ---- pass 2: normalised scores, written row-contiguously
+  const float scale = invZ * wgt;
+  const float Lm0 = Lm == -INFINITY ? 0.f : Lm;  // no valid unit at all: every value is 0
+  // the column tile's rows of S through a buffer resource that ends at its
+  // last valid query block; stores past it, or flagged with an offset beyond
+  // any record, are dropped
+  const int rows_valid = max(0, min(QBT, a.nQB - qb0));
+  const uint64_t sb = reinterpret_cast<uint64_t>(a.S + (static_cast<size_t>(bh) * a.nQB + min(qb0, a.nQB)) * a.nKU);
+  // uniform: a scalar resource. readfirstlane returns int: each half goes
+  // through uint32_t, so that the low half is not sign-extended into the high
+  const uint64_t sb_u =
+      (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sb >> 32)))) << 32) |
+      static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(sb & 0xffffffffu))));
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<float*>(sb_u), 0, __builtin_amdgcn_readfirstlane(rows_valid * a.nKU * 4), BUFFER_WORD3);
+  float* trow = &tile[wave][ibt][0];
+  sweep([&](int ch, const f32x16& acc) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = __builtin_amdgcn_exp2f(acc[r] - Lm0) * scale;  // exp2(-inf) = 0
+    group_reduce_scatter<G>(v, grp);  // sums over the G representatives of the query block
+    // the lane's sums are consecutive units of its query block's row
+    if constexpr (G == 2) {
+      *reinterpret_cast<f32x4*>(trow + 16 * grp + 4 * h) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(trow + 16 * grp + 8 + 4 * h) = f32x4{v[4], v[5], v[6], v[7]};
+    } else if constexpr (G == 4) {
+      *reinterpret_cast<f32x4*>(trow + 8 * grp + 4 * h) = f32x4{v[0], v[1], v[2], v[3]};
+    } else {
+      *reinterpret_cast<f32x2*>(trow + 8 * (grp / 2) + 4 * h + 2 * (grp % 2)) = f32x2{v[0], v[1]};
+    }
+    // the block is exchanged between the lanes of this wave only
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int col = ch * 32 + n;
+#pragma unroll
+    for (int k = 0; k < QBT / 2; ++k) {
+      const int row = 2 * k + h;  // query block qb0 + row
+      const uint32_t off = col < a.nKU ? static_cast<uint32_t>(row * a.nKU + col) * 4u : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tile[wave][row][n]), srs, off, 0, 0);
+    }
+    // the next chunk's writes to the block wait for these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }, [&] {
+    // as many stores as a chunk issues, all dropped (offset beyond any
+    // record): every entry to the chunk loop then has them behind the loads,
+    // and the wait for the loads leaves S stores in flight
+#pragma unroll
+    for (int k = 0; k < QBT / 2; ++k) __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0x80000000u + 4u * k, 0, 0);
+  });
+}
+
 }  // namespace
 
 hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, const int32_t* perm,
@@ -421,8 +722,15 @@ hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, cons
     }
     return hipGetLastError();
   }
-#define BSA_SCORES(D, G)                                                                  \
-  if (cache) hipLaunchKernelGGL((scores_kernel<D, G, true, false>), grid, block, 0, s, a); \
+  // two or more representatives per query block: the kernel that shares each
+  // staged chunk of key means between four column tiles
+  const int per_wg_shared = SS_CT * 32 / groups;
+  const dim3 grid_shared(g.B * g.H * ((g.nQB + per_wg_shared - 1) / per_wg_shared));
+  ScoreArgs as = a;
+  as.n_qgroups = (g.nQB + per_wg_shared - 1) / per_wg_shared;
+#define BSA_SCORES(D, G)                                                                                \
+  if (G > 1) hipLaunchKernelGGL((scores_shared_kernel<D, (G > 1 ? G : 2)>), grid_shared, block, 0, s, as); \
+  else if (cache) hipLaunchKernelGGL((scores_kernel<D, G, true, false>), grid, block, 0, s, a);         \
   else hipLaunchKernelGGL((scores_kernel<D, G, false, false>), grid, block, 0, s, a)
 #define BSA_SCORES_G(D)                      \
   switch (groups) {                          \
