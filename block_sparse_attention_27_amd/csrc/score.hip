@@ -30,6 +30,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int MEAN_THREADS = 256;
 
@@ -371,9 +372,13 @@ constexpr int SS_CT = 4;  // column tiles per workgroup
 constexpr int SS_US = 2;  // unit halves per workgroup
 constexpr int SS_LT = 36; // row stride (floats) of a wave's transposition tile: 16-byte aligned rows
 
-template <int D>
-__device__ __forceinline__ int kmean_swz(int unit) {  // 16-byte chunk swizzle of a bf16 row of D
-  return D == 128 ? (unit & 15) : ((unit >> 1) & 7);
+// bf16 hi + lo parts of two floats, packed: hi = bf16(x), lo = bf16(x - hi)
+// (one conversion per pair and part)
+__device__ __forceinline__ void split2_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  const f32x2 hf = __builtin_convertvector(h, f32x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - hf[0], b - hf[1]}, bf16x2));
 }
 
 // One step of a reduce-scatter over lane pairs (lane, partner given by the DPP
@@ -426,8 +431,11 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs 
   constexpr int QBT = 32 / G;       // query blocks per column tile
   constexpr int QBW = CT * QBT;     // query blocks per workgroup
   constexpr int PER = 32 * D / 4 / (64 * CT);  // float4 loads per thread and chunk
-  // [buffer][unit half][hi, lo][unit][d], bf16, 16-byte chunks of a row swizzled
-  __shared__ __align__(16) uint16_t kbuf[2][US][2][32 * D];
+  // [buffer][unit half][hi, lo][unit][d], bf16; rows padded by 16 bytes, so
+  // that the 16 lanes of a fragment read (rows n, one 16-byte slot each) fall
+  // in distinct banks
+  constexpr int KR = D + 8;
+  __shared__ __align__(16) uint16_t kbuf[2][US][2][32 * KR];
   __shared__ float red_m[SC_WAVES][32];
   __shared__ float red_s[SC_WAVES][32];
   __shared__ __align__(16) float tile[SC_WAVES][QBT][SS_LT];
@@ -447,12 +455,15 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs 
   const bool qok = qb < a.nQB;
   const size_t rep = (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * G;
   const float* qm = a.q_rep + (rep + grp) * D + 8 * h;
+  // the representatives carry the scale to log2 units (sm_scale log2 e), so
+  // the products are the logits
+  const float c2 = a.sm_scale * 1.4426950408889634f;
   bf16x8 qhi[D / 16], qlo[D / 16];
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
     const f32x4 x0 = qok ? *reinterpret_cast<const f32x4*>(qm + 16 * st) : f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 x1 = qok ? *reinterpret_cast<const f32x4*>(qm + 16 * st + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    split_bf16(x0, x1, qhi[st], qlo[st]);
+    split_bf16(x0 * c2, x1 * c2, qhi[st], qlo[st]);
   }
   // weight n_g / n of this lane's representative; a block with no valid row
   // scores with its first (zero) representative alone
@@ -473,7 +484,6 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs 
       const_cast<float*>(a.k_mean + static_cast<size_t>(bh) * a.nKU * D), 0, a.nKU * D * 4, BUFFER_WORD3);
   const int n_chunks = (a.nKU + 31) / 32;
   const int n_iter = (n_chunks + US - 1) / US;  // the same count for every wave: the barriers match
-  const float c2 = a.sm_scale * 1.4426950408889634f;
   // units 0 .. nV - 1 hold keys, all block_k of them but the last
   const int nV = min(a.nKU, (a.N + a.block_k - 1) / a.block_k);
   const int ch_edge = nV > 0 ? (nV - 1) / 32 : 0;  // chunks from here on hold the last valid unit or none
@@ -495,47 +505,37 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs 
     for (int p = 0; p < PER; ++p) {
       const int idx = gt + 64 * CT * p, unit = idx / (D / 4), d4 = idx % (D / 4);
       uint32_t hi[2], lo[2];
-#pragma unroll
-      for (int z = 0; z < 2; ++z) {
-        const float x0 = xk[p][2 * z], x1 = xk[p][2 * z + 1];
-        const __bf16 h0 = static_cast<__bf16>(x0), h1 = static_cast<__bf16>(x1);
-        const __bf16 l0 = static_cast<__bf16>(x0 - static_cast<float>(h0));
-        const __bf16 l1 = static_cast<__bf16>(x1 - static_cast<float>(h1));
-        hi[z] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
-                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
-        lo[z] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l0)) |
-                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l1)) << 16);
-      }
-      // element 4 d4 of the row: 16-byte chunk d4 / 2 (swizzled), 8-byte half d4 % 2
-      const int off = unit * D + 8 * ((d4 / 2) ^ kmean_swz<D>(unit)) + 4 * (d4 % 2);
-      *reinterpret_cast<u32x2*>(&kbuf[buf][us][0][off]) = u32x2{hi[0], hi[1]};
-      *reinterpret_cast<u32x2*>(&kbuf[buf][us][1][off]) = u32x2{lo[0], lo[1]};
+      split2_bf16(xk[p][0], xk[p][1], hi[0], lo[0]);
+      split2_bf16(xk[p][2], xk[p][3], hi[1], lo[1]);
+      *reinterpret_cast<u32x2*>(&kbuf[buf][us][0][unit * KR + 4 * d4]) = u32x2{hi[0], hi[1]};
+      *reinterpret_cast<u32x2*>(&kbuf[buf][us][1][unit * KR + 4 * d4]) = u32x2{lo[0], lo[1]};
     }
   };
-  // x for the 32 units of chunk ch (register r: unit ch 32 + 8 (r/4) + 4 h + r%4)
-  // in log2 units, with the key-count offset; -inf for units with no valid key.
-  // The A operand is row n of the staged chunk; every fragment is read before
+  // products of the chunk in buffer buf with this wave's representatives
+  // (kh.qh + kh.ql + kl.qh, one fp32 accumulator): the logits in log2 units.
+  // The A operand is row n of the staged chunk, all 16 fragments read before
   // the first product.
-  auto logits = [&](int ch, int buf) {
-    const uint16_t* kh = &kbuf[buf][us][0][n * D];
-    const uint16_t* kl = &kbuf[buf][us][1][n * D];
-    const int sw = kmean_swz<D>(n);
+  auto products = [&](int buf, f32x16& p0) {
+    const uint16_t* kh = &kbuf[buf][us][0][n * KR + 8 * h];
+    const uint16_t* kl = &kbuf[buf][us][1][n * KR + 8 * h];
     bf16x8 khi[D / 16], klo[D / 16];
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      const int c = (2 * st + h) ^ sw;
-      khi[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kh + 8 * c));
-      klo[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + 8 * c));
+      khi[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kh + 16 * st));
+      klo[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + 16 * st));
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
-    f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+    p0 = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[st], qhi[st], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[st], qlo[st], acc1, 0, 0, 0);
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo[st], qhi[st], acc0, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[st], qhi[st], p0, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[st], qlo[st], p0, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo[st], qhi[st], p0, 0, 0, 0);
     }
-    f32x16 acc = (acc0 + acc1) * c2;
+  };
+  // x for the 32 units of chunk ch (register r: unit ch 32 + 8 (r/4) + 4 h + r%4)
+  // in log2 units, with the key-count offset; -inf for units with no valid key
+  auto logits = [&](int ch, const f32x16& p0) {
+    f32x16 acc = p0;
     if (ch >= ch_edge) {  // uniform: the chunk of the last valid unit and any after it
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -546,44 +546,75 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs 
     return acc;
   };
 
-  // one pass over this unit half's chunks. The chunk of iteration it sits in
-  // buffer it & 1: a buffer is rewritten two iterations later, after the
-  // barrier that follows its reads. A chunk past the last (the second unit
-  // half's final iteration when the chunk count is odd, and the load after
-  // every half's last chunk) reads zeros; its units all get -inf logits, so
-  // body(ch, acc) adds nothing and stores nothing for it. Loads and bodies
-  // are unconditional, so that the wait for a chunk's loads leaves the stores
-  // of S issued after them in flight.
-  auto sweep = [&](auto&& body, auto&& after_first_load) {
+  // One pass over this unit half's chunks, software-pipelined. Chunk i sits
+  // in buffer i & 1. After the barrier that ends iteration it - 1, iteration
+  // it issues the products of chunk it + 1 between the exponentials of chunk
+  // it (valu) and the staging of chunk it + 2 (loaded during iteration it - 1)
+  // into the buffer chunk it left, starts the load of chunk it + 3, then
+  // stores chunk it's results (store). A buffer is rewritten only behind the
+  // barrier that follows the products reading it. A chunk past the last (the
+  // second unit half's final chunk when the chunk count is odd, and the loads
+  // and products ahead of every half's last chunk) reads zeros; its units
+  // all get -inf logits, so valu adds nothing and store stores nothing for it.
+  // Loads and stores are unconditional, so that the wait for a chunk's loads
+  // leaves the stores of S issued after them in flight; prime issues as many
+  // (dropped) stores on the way in.
+  auto sweep = [&](auto&& valu, auto&& store, auto&& prime) {
+    f32x16 p0;
     load_chunk(us);
-    after_first_load();
+    store_chunk(0);
+    load_chunk(us + US);
+    store_chunk(1);
+    load_chunk(us + 2 * US);
+    prime();
+    __syncthreads();
+    products(0, p0);
+    f32x16 cur = logits(us, p0);
+    __syncthreads();  // buffer 0 is rewritten in the first iteration
     for (int it = 0; it < n_iter; ++it) {
       const int ch = us + it * US;
+      // keeps the work of chunk it below the barrier, next to the products
+      // it is interleaved with (pure arithmetic may otherwise move up into
+      // the previous iteration)
+      asm volatile("" : "+v"(cur));
+      products((it + 1) & 1, p0);
+      const auto r = valu(ch, cur);
       store_chunk(it & 1);
-      load_chunk(ch + US);
+      load_chunk(ch + 3 * US);
+      // the 16 fragment reads, then each product followed by other work
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);
+#pragma unroll
+      for (int x = 0; x < 3 * (D / 16); ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      store(ch, r);
+      cur = logits(ch + US, p0);
       __syncthreads();
-      body(ch, logits(ch, it & 1));
     }
-    __syncthreads();  // the last buffers are read before the next sweep rewrites them
   };
 
   // ---- pass 1: running maximum and sum per representative
   float run_m = -INFINITY, run_s = 0.f;
-  sweep([&](int, const f32x16& acc) {
-    float lmax = acc[0];
+  sweep(
+      [&](int, const f32x16& acc) {
+        float lmax = acc[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) lmax = fmaxf(lmax, acc[r]);
-    // a chunk with no valid unit leaves the state as it is; otherwise nm is
-    // finite and exp2(-inf - nm) = 0 drops the invalid units
-    if (lmax != -INFINITY) {
-      const float nm = fmaxf(run_m, lmax);
-      float sv = run_s * __builtin_amdgcn_exp2f(run_m - nm);  // run_s = 0 while run_m = -inf
+        for (int r = 1; r < 16; ++r) lmax = fmaxf(lmax, acc[r]);
+        // no branch: a chunk with no valid unit (lmax = -inf) leaves the state
+        // as it is, and exp2(-inf) = 0 drops invalid units and an empty state
+        const float nm = fmaxf(run_m, lmax);
+        const float ns = nm == -INFINITY ? 0.f : nm;
+        float sv = run_s * __builtin_amdgcn_exp2f(run_m - ns);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv += __builtin_amdgcn_exp2f(acc[r] - nm);
-      run_s = sv;
-      run_m = nm;
-    }
-  }, [] {});
+        for (int r = 0; r < 16; ++r) sv += __builtin_amdgcn_exp2f(acc[r] - ns);
+        run_s = sv;
+        run_m = nm;
+        return sv;
+      },
+      // nothing to store; consuming the sum here keeps its exponent work
+      // next to the products instead of sinking below the next chunk's mask
+      [](int, float sv) { asm volatile("" ::"v"(sv)); }, [] {});
   {  // the two lane halves, then the unit halves of the column tile
     const float om = __shfl_xor(run_m, 32), os = __shfl_xor(run_s, 32);
     const float nm = fmaxf(run_m, om);
@@ -623,42 +654,48 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs 
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       reinterpret_cast<float*>(sb_u), 0, __builtin_amdgcn_readfirstlane(rows_valid * a.nKU * 4), BUFFER_WORD3);
   float* trow = &tile[wave][ibt][0];
-  sweep([&](int ch, const f32x16& acc) {
+  struct Sums {
     float v[16];
+  };
+  sweep(
+      [&](int, const f32x16& acc) {
+        Sums o;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = __builtin_amdgcn_exp2f(acc[r] - Lm0) * scale;  // exp2(-inf) = 0
-    group_reduce_scatter<G>(v, grp);  // sums over the G representatives of the query block
-    // the lane's sums are consecutive units of its query block's row
-    if constexpr (G == 2) {
-      *reinterpret_cast<f32x4*>(trow + 16 * grp + 4 * h) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(trow + 16 * grp + 8 + 4 * h) = f32x4{v[4], v[5], v[6], v[7]};
-    } else if constexpr (G == 4) {
-      *reinterpret_cast<f32x4*>(trow + 8 * grp + 4 * h) = f32x4{v[0], v[1], v[2], v[3]};
-    } else {
-      *reinterpret_cast<f32x2*>(trow + 8 * (grp / 2) + 4 * h + 2 * (grp % 2)) = f32x2{v[0], v[1]};
-    }
-    // the block is exchanged between the lanes of this wave only
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int col = ch * 32 + n;
+        for (int r = 0; r < 16; ++r) o.v[r] = __builtin_amdgcn_exp2f(acc[r] - Lm0) * scale;  // exp2(-inf) = 0
+        group_reduce_scatter<G>(o.v, grp);  // sums over the G representatives of the query block
+        return o;
+      },
+      [&](int ch, const Sums& o) {
+        // the lane's sums are consecutive units of its query block's row
+        if constexpr (G == 2) {
+          *reinterpret_cast<f32x4*>(trow + 16 * grp + 4 * h) = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
+          *reinterpret_cast<f32x4*>(trow + 16 * grp + 8 + 4 * h) = f32x4{o.v[4], o.v[5], o.v[6], o.v[7]};
+        } else if constexpr (G == 4) {
+          *reinterpret_cast<f32x4*>(trow + 8 * grp + 4 * h) = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
+        } else {
+          *reinterpret_cast<f32x2*>(trow + 8 * (grp / 2) + 4 * h + 2 * (grp % 2)) = f32x2{o.v[0], o.v[1]};
+        }
+        // the block is exchanged between the lanes of this wave only
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int col = ch * 32 + n;
 #pragma unroll
-    for (int k = 0; k < QBT / 2; ++k) {
-      const int row = 2 * k + h;  // query block qb0 + row
-      const uint32_t off = col < a.nKU ? static_cast<uint32_t>(row * a.nKU + col) * 4u : 0x80000000u;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tile[wave][row][n]), srs, off, 0, 0);
-    }
-    // the next chunk's writes to the block wait for these reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }, [&] {
-    // as many stores as a chunk issues, all dropped (offset beyond any
-    // record): every entry to the chunk loop then has them behind the loads,
-    // and the wait for the loads leaves S stores in flight
+        for (int k = 0; k < QBT / 2; ++k) {
+          const int row = 2 * k + h;  // query block qb0 + row
+          const uint32_t off = col < a.nKU ? static_cast<uint32_t>(row * a.nKU + col) * 4u : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tile[wave][row][n]), srs, off, 0, 0);
+        }
+        // the next chunk's writes to the block wait for these reads
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      },
+      [&] {
+        // as many stores as a chunk issues, all dropped (offset beyond any record)
 #pragma unroll
-    for (int k = 0; k < QBT / 2; ++k) __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0x80000000u + 4u * k, 0, 0);
-  });
+        for (int k = 0; k < QBT / 2; ++k) __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0x80000000u + 4u * k, 0, 0);
+      });
 }
 
 }  // namespace
