@@ -396,13 +396,17 @@ __device__ __forceinline__ void scatter_step(float (&v)[16], bool upper) {
 
 // Sums v (16 values, index 4 m + e) over the G consecutive lanes of a group,
 // each lane keeping 16 / G of the sums in v[0 .. 16 / G - 1]:
+//   G = 1: m = i / 4, e = i % 4 (nothing to sum);
 //   G = 2: m = 2 grp + i / 4, e = i % 4;  G = 4: m = grp, e = i;
 //   G = 8: m = grp / 2, e = 2 (grp % 2) + i.
 // The partners are lane xor 1 and xor 2 (quad permutations) and, for G = 8,
 // the mirror lane 7 - i of an 8-lane half-row (it lies in the other quad).
 template <int G>
 __device__ __forceinline__ void group_reduce_scatter(float (&v)[16], int grp) {
-  if constexpr (G == 2) {
+  if constexpr (G == 1) {
+    (void)v;
+    (void)grp;
+  } else if constexpr (G == 2) {
     scatter_step<0xB1, 16>(v, grp & 1);
   } else if constexpr (G == 4) {
     scatter_step<0x4E, 16>(v, grp & 2);
@@ -415,7 +419,8 @@ __device__ __forceinline__ void group_reduce_scatter(float (&v)[16], int grp) {
   }
 }
 
-// Score matrix for G >= 2 representatives per query block. The eight waves
+// Score matrix for G representatives per query block (G >= 2, or G = 1 when
+// the logits of a row do not fit the LDS cache of scores_kernel). The eight waves
 // form four column tiles x two unit halves: wave (ct, us) owns MFMA columns
 // (representatives) 32 ct .. 32 ct + 31 of the workgroup's 128 and the unit
 // chunks us, us + 2, ... The four waves of a unit half load each chunk of 32
@@ -427,7 +432,7 @@ __device__ __forceinline__ void group_reduce_scatter(float (&v)[16], int grp) {
 template <int D, int G>
 __global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs a) {
   constexpr int CT = SS_CT, US = SS_US;
-  static_assert(CT * US == SC_WAVES && G >= 2, "wave split");
+  static_assert(CT * US == SC_WAVES && (G == 1 || G == 2 || G == 4 || G == 8), "wave split");
   constexpr int QBT = 32 / G;       // query blocks per column tile
   constexpr int QBW = CT * QBT;     // query blocks per workgroup
   constexpr int PER = 32 * D / 4 / (64 * CT);  // float4 loads per thread and chunk
@@ -667,7 +672,11 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_shared_kernel(ScoreArgs 
       },
       [&](int ch, const Sums& o) {
         // the lane's sums are consecutive units of its query block's row
-        if constexpr (G == 2) {
+        if constexpr (G == 1) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            *reinterpret_cast<f32x4*>(trow + 8 * m + 4 * h) = f32x4{o.v[4 * m], o.v[4 * m + 1], o.v[4 * m + 2], o.v[4 * m + 3]};
+        } else if constexpr (G == 2) {
           *reinterpret_cast<f32x4*>(trow + 16 * grp + 4 * h) = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
           *reinterpret_cast<f32x4*>(trow + 16 * grp + 8 + 4 * h) = f32x4{o.v[4], o.v[5], o.v[6], o.v[7]};
         } else if constexpr (G == 4) {
@@ -759,14 +768,15 @@ hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, cons
     }
     return hipGetLastError();
   }
-  // two or more representatives per query block: the kernel that shares each
-  // staged chunk of key means between four column tiles
+  // two or more representatives per query block, or one when the logits do
+  // not fit the LDS cache: the kernel that shares each staged chunk of key
+  // means between four column tiles
   const int per_wg_shared = SS_CT * 32 / groups;
   const dim3 grid_shared(g.B * g.H * ((g.nQB + per_wg_shared - 1) / per_wg_shared));
   ScoreArgs as = a;
   as.n_qgroups = (g.nQB + per_wg_shared - 1) / per_wg_shared;
 #define BSA_SCORES(D, G)                                                                                \
-  if (G > 1) hipLaunchKernelGGL((scores_shared_kernel<D, (G > 1 ? G : 2)>), grid_shared, block, 0, s, as); \
+  if (G > 1 || !cache) hipLaunchKernelGGL((scores_shared_kernel<D, G>), grid_shared, block, 0, s, as);    \
   else if (cache) hipLaunchKernelGGL((scores_kernel<D, G, true, false>), grid, block, 0, s, a);         \
   else hipLaunchKernelGGL((scores_kernel<D, G, false, false>), grid, block, 0, s, a)
 #define BSA_SCORES_G(D)                      \

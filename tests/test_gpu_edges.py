@@ -208,6 +208,29 @@ def test_determinism_bitwise():
         assert torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
 
 
+@pytest.mark.parametrize("d,bq,dtype,perm", [(64, 64, "fp32", False), (128, 128, "bf16", True)])
+def test_scores_more_units_than_the_logit_cache(d, bq, dtype, perm):
+    # 655 key units of 32 (the last holds 23 keys) is more than the 640 whose logits the one-representative
+    # score kernel keeps in LDS: the score pass then runs on the kernel that stages the key means once per
+    # workgroup, with a ragged last workgroup of query blocks
+    print_case(f"scores with 655 units d={d} bq={bq} {dtype} perm={perm}")
+    w = Workload("units", B=1, H=2, grid=(7, 41, 73), d=d, dtype=dtype, block_q=bq, block_k=32,
+                 k_exact=2, m_sample=3, clusters=6, temperature=1.0, permute=perm, seed=12)
+    assert w.n_valid_units == 655 and w.N % 32 == 23
+    g = generate(w)
+    q, k = to_device(g["q"]), to_device(g["k"])
+    pm = torch.from_numpy(g["perm"]).cuda() if g["perm"] is not None else None
+    p = bsa.problem_for(w)
+    S, qm, km = bsa.score(p, q, k, pm)
+    torch.cuda.synchronize()
+    qh, kh = host_f64(g["q"]), host_f64(g["k"])
+    S_ref, qb, kb = oracle.score(qh, kh, w.N, w.block_q, w.block_k, w.sm_scale, g["perm"])
+    Sg = S.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(Sg - S_ref) <= 1e-3 * S_ref + 1e-12 * S_ref.max(-1, keepdims=True))
+    assert np.all(Sg[..., w.n_valid_units:] == 0)
+    assert rel_l2(qm.cpu().numpy(), qb) < 1e-5 and rel_l2(km.cpu().numpy(), kb) < 1e-5
+
+
 @pytest.mark.parametrize("perm", [False, True])
 def test_lists_longer_than_one_chunk(perm):
     # 1,100 list entries per query block: the attention kernel takes them in two sorted chunks
