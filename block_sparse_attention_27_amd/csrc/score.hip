@@ -419,8 +419,9 @@ __device__ __forceinline__ void group_reduce_scatter(float (&v)[16], int grp) {
   }
 }
 
-// Score matrix for G representatives per query block (G >= 2, or G = 1 when
-// the logits of a row do not fit the LDS cache of scores_kernel). The eight waves
+// Score matrix for G representatives per query block (G >= 2; G = 1 unless
+// the grid would be small and the logits fit the LDS cache of scores_kernel).
+// The eight waves
 // form four column tiles x two unit halves: wave (ct, us) owns MFMA columns
 // (representatives) 32 ct .. 32 ct + 31 of the workgroup's 128 and the unit
 // chunks us, us + 2, ... The four waves of a unit half load each chunk of 32
@@ -768,15 +769,17 @@ hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, cons
     }
     return hipGetLastError();
   }
-  // two or more representatives per query block, or one when the logits do
-  // not fit the LDS cache: the kernel that shares each staged chunk of key
-  // means between four column tiles
+  // the kernel that shares each staged chunk of key means between four
+  // column tiles: two or more representatives per query block; one when the
+  // logits do not fit the LDS cache, or when its grid still has 64 or more
+  // workgroups (below that, scores_kernel's four times larger grid is faster)
   const int per_wg_shared = SS_CT * 32 / groups;
   const dim3 grid_shared(g.B * g.H * ((g.nQB + per_wg_shared - 1) / per_wg_shared));
   ScoreArgs as = a;
   as.n_qgroups = (g.nQB + per_wg_shared - 1) / per_wg_shared;
+  const bool shared_one = !cache || grid_shared.x >= 64;
 #define BSA_SCORES(D, G)                                                                                \
-  if (G > 1 || !cache) hipLaunchKernelGGL((scores_shared_kernel<D, G>), grid_shared, block, 0, s, as);    \
+  if (G > 1 || shared_one) hipLaunchKernelGGL((scores_shared_kernel<D, G>), grid_shared, block, 0, s, as); \
   else if (cache) hipLaunchKernelGGL((scores_kernel<D, G, true, false>), grid, block, 0, s, a);         \
   else hipLaunchKernelGGL((scores_kernel<D, G, false, false>), grid, block, 0, s, a)
 #define BSA_SCORES_G(D)                      \
