@@ -17,7 +17,10 @@
 // parts (three products, fp32 accumulation: about 1e-5 relative), so each
 // lane keeps its own running max and n_j-weighted sum; a second pass
 // recomputes the logits (or reads them back from LDS) and writes S once,
-// normalised.
+// normalised. scores_shared_kernel does the same with each staged chunk of key
+// means shared by four column tiles of a workgroup; it takes the clustering
+// scorer's G representatives per block, and one representative whenever its
+// grid is large enough.
 #include "bsa_internal.hpp"
 
 #include <math.h>
