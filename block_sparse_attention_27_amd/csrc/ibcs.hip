@@ -390,33 +390,30 @@ __global__ __launch_bounds__(CL_THREADS, BF16 ? (G <= 4 ? 6 : 5) : 1) void block
   // ---- representatives: fp32 means of the original rows of every group
   if constexpr (BF16) {
     // one-hot times the bf16 rows on MFMA with fp32 sums (a fixed order:
-    // deterministic). The B operand of a 16-row step is column 32 nt + n of
-    // rows r0 + {4 h .. 4 h + 3, 8 + 4 h .. 8 + 4 h + 3}, the row order of the
-    // one-hot operand, read from global memory.
+    // deterministic). The rows are read again (the block was read at the
+    // start: L2) with the staging's 16-byte loads into the fixed-point rows'
+    // LDS, free after the last iteration, and the B operand of a 16-row step
+    // (column 32 nt + n of rows r0 + {4 h .. 4 h + 3, 8 + 4 h .. 8 + 4 h + 3},
+    // the row order of the one-hot operand) comes from the transposing reads
+    // of the centroid sums.
+    uint16_t* rb = reinterpret_cast<uint16_t*>(&qh[0][0]);
+#pragma unroll
+    for (int pp = 0; pp < MAXP; ++pp) {
+      const int r = rg + pp * RPP;
+      const int gr = grow[r];
+      const u32x4 x = gr >= 0 ? *reinterpret_cast<const u32x4*>(base + (static_cast<size_t>(gr) * D + cc * EPC) * ESZ)
+                              : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(rb + r * LQ + cc * EPC) = x;
+    }
+    __syncthreads();  // the rows are staged
     const int nt = wave % NT, kp = wave / NT;
     const bool gok = ln < G;
-    const uint16_t* qcol = static_cast<const uint16_t*>(a.q) + static_cast<size_t>(bh) * a.N_pad * D + 32 * nt + ln;
-    u16x2 xv[KPW][4];  // pairs of rows: both halves of a register come from 16-bit loads
-#pragma unroll
-    for (int kk = 0; kk < KPW; ++kk) {
-      const int r0 = 16 * (kp * KPW + kk);
-#pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        const int e0 = 2 * z, e1 = 2 * z + 1;
-        const int g0 = grow[r0 + (e0 < 4 ? 4 * lh + e0 : 8 + 4 * lh + e0 - 4)];
-        const int g1 = grow[r0 + (e1 < 4 ? 4 * lh + e1 : 8 + 4 * lh + e1 - 4)];
-        xv[kk][z] = u16x2{g0 >= 0 ? qcol[static_cast<size_t>(g0) * D] : static_cast<uint16_t>(0),
-                          g1 >= 0 ? qcol[static_cast<size_t>(g1) * D] : static_cast<uint16_t>(0)};
-      }
-    }
     f32x16 acc = {};
 #pragma unroll
     for (int kk = 0; kk < KPW; ++kk) {
       const int r0 = 16 * (kp * KPW + kk);
       const u32x4 au = row8_tr_order(&ohb[gok ? ln : 0][0], r0, lane, gok);
-      u32x4 bu;
-#pragma unroll
-      for (int z = 0; z < 4; ++z) bu[z] = __builtin_bit_cast(uint32_t, xv[kk][z]);
+      const u32x4 bu = column8<LQ>(rb, r0, 32 * nt, lane);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, au), __builtin_bit_cast(bf16x8, bu), acc,
                                                     0, 0, 0);
     }
