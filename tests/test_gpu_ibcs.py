@@ -149,3 +149,21 @@ def test_ibcs_last_block_with_fewer_rows_than_groups(bq, groups, dtype):
     _check_blocks(blocks, S, qc, qs, ref, n_rows, -(-w.N // 64))
     tail = qs[0, :, last]
     assert np.all(tail.sum(-1) == 2) and np.all((tail > 0).sum(-1) <= 2)
+
+
+@pytest.mark.parametrize("d,bq,groups,dtype,perm", [(64, 64, 8, "bf16", True), (128, 128, 2, "fp32", False)])
+def test_ibcs_many_key_units(d, bq, groups, dtype, perm):
+    # 656 key units of 32 (21 chunks of 32: the score loop's steady state with an odd chunk count; the last unit
+    # holds 23 keys) and a ragged last workgroup of query blocks, every block against the oracle
+    print_case(f"ibcs with 656 units d={d} bq={bq} G={groups} {dtype} perm={perm}")
+    w = Workload("ibcs_units", B=1, H=2, grid=(7, 41, 73), d=d, dtype=dtype, block_q=bq, block_k=32,
+                 k_exact=2, m_sample=3, clusters=6, temperature=1.0, permute=perm, seed=13)
+    assert w.N_pad // 32 == 656 and w.N % 32 == 23
+    p, (q, k, pm), (S, qc, qs, km) = _run(w, groups, 2)
+    S_ref, c_ref, z_ref, kb = oracle.score_ibcs(host_f64(q), host_f64(k), w.N, bq, 32, w.sm_scale, groups, 2, pm)
+    assert rel_l2(km, kb) < 1e-5
+    nQB = p.N_pad // bq
+    blocks = [(0, h, i) for h in range(w.H) for i in range(nQB)]
+    ref = ([S_ref[x] for x in blocks], [c_ref[x] for x in blocks], [z_ref[x] for x in blocks])
+    _check_blocks(blocks, S, qc, qs, ref, oracle.valid_counts(w.N, p.N_pad, bq), w.n_valid_units)
+
