@@ -1,9 +1,13 @@
 // Weighted block-sparse flash attention (and its dense special case) on bf16
-// MFMA for gfx950: launch and dispatch over the kernel variants
-// (attend_bf16_w32.hpp). Instantiated per head dimension in
+// MFMA for gfx950: launch and dispatch over the kernel variants. 128-row query
+// blocks run attend_t64_kernel (attend_bf16_t64.hpp: 4-wave workgroups, two
+// per CU, 64-key tiles); 64-row blocks run attend_w32_kernel
+// (attend_bf16_w32.hpp: one 4-wave workgroup per CU, 128-key tiles split
+// between two waves per row group). Instantiated per head dimension in
 // attend_bf16_d128.hip and attend_bf16_d64.hip.
 #pragma once
 
+#include "attend_bf16_t64.hpp"
 #include "attend_bf16_w32.hpp"
 
 namespace bsa {
@@ -11,7 +15,11 @@ namespace attend_bf16_impl {
 
 template <int D, int BQ, int BK, bool DENSE, bool PERM, bool OUT32>
 hipError_t launch_one(const AttendArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attend_w32_kernel<D, BQ, BK, DENSE, PERM, OUT32>), dim3(a.n_wg), dim3(BQ * 4), 0, s, a);
+  if constexpr (BQ == 128) {
+    hipLaunchKernelGGL((attend_t64_kernel<D, BK, DENSE, PERM, OUT32>), dim3(a.n_wg), dim3(64 * NW64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attend_w32_kernel<D, BQ, BK, DENSE, PERM, OUT32>), dim3(a.n_wg), dim3(BQ * 4), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -9,7 +9,8 @@
 //                              S^T accumulators after exp and bf16 packing)
 // on v_mfma_f32_32x32x16_bf16. A lane holds one query row, so the row max and
 // row sum stay in the lane except for one exchange between 32-lane halves.
-// Used for 64-row query blocks (4 waves, one per SIMD).
+// Used for 64-row query blocks (4 waves, one per SIMD); 128-row blocks take
+// attend_t64_kernel (attend_bf16_t64.hpp).
 #pragma once
 
 #include "attend_common.hpp"

@@ -1,8 +1,8 @@
 // Helpers shared by the bf16 MFMA attention kernels for gfx950 (the
-// 32-row-per-wave kernel in attend_bf16_w32.hpp and the 64-row-per-wave
-// kernel in attend_bf16_w64.hpp): tile staging from global memory into LDS,
-// list sorting and tile descriptions, LDS read addressing, masking and row
-// reductions.
+// 128-row-block kernel with two workgroups per CU in attend_bf16_t64.hpp and
+// the 64-row-block kernel in attend_bf16_w32.hpp): tile staging from global
+// memory into LDS, list sorting and tile descriptions, LDS read addressing,
+// masking and row reductions.
 //
 // What the kernels compute (AB-Attention, Abstract and transcript on the
 // tiled kernel; InstaGen, Abstract): for the query rows of one query block and
@@ -12,7 +12,7 @@
 // with x_rt = sm_scale * log2(e) * <q_r, k_t>, and out_r = num_r / den_r. The
 // weight enters as an additive shift log2(w_j) of the exponent, folded into the
 // per-row subtraction constant, so it costs nothing per element. Key units
-// smaller than the 128-key tile (32 or 64 keys) are gathered into one tile.
+// smaller than a tile are gathered into one tile.
 //
 // Data movement. K and V tiles go from global memory straight into LDS
 // (global_load_lds_dwordx4, no registers), double-buffered so the next tile
@@ -44,7 +44,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define BSA_LDS __attribute__((address_space(3)))
 
-constexpr int TILE = 128;           // keys per staged tile
+constexpr int TILE = 128;           // keys per staged tile of attend_w32_kernel
 constexpr int LMAX = 1024;          // list entries sorted and held in LDS at a time
 constexpr float RESCALE_SLACK = 8;  // log2 units the running max may lag the true max
 
@@ -109,7 +109,7 @@ __device__ __forceinline__ int pick4(const int (&x)[4], int u) {
   return u == 0 ? x[0] : u == 1 ? x[1] : u == 2 ? x[2] : x[3];
 }
 
-// Direct global -> LDS staging of one 128-key tile of K or V. A wave
+// Direct global -> LDS staging of one tile (TK keys) of K or V. A wave
 // instruction moves 1 KB = RPI whole rows; lane l lands at byte 16 l of it,
 // i.e. in row l / CPR at physical chunk l % CPR, which holds logical chunk
 // (l % CPR) ^ swz(row). Instruction i of wave w covers tile rows
@@ -119,18 +119,18 @@ __device__ __forceinline__ int pick4(const int (&x)[4], int u) {
 // tensors' tiles: one per-lane register each for K and V, and the rest of the
 // address (the unit's first row, the instruction's row step) is uniform.
 // Rows of one instruction never straddle a unit (BK is a multiple of RPI).
-template <int D, int NW>
+template <int D, int NW, int TK = TILE>
 struct StageGeom {
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int RPI = 1024 / (2 * D);   // rows per instruction
   static constexpr int G = NW * RPI;           // row step between a wave's instructions
-  static constexpr int PER_WAVE = TILE / G;    // instructions per wave and tile
-  static_assert(G % 16 == 0 && TILE % G == 0, "swizzle periods must divide the row step");
+  static constexpr int PER_WAVE = TK / G;      // instructions per wave and tile of TK keys
+  static_assert(G % 16 == 0 && TK % G == 0, "swizzle periods must divide the row step");
 };
 
-template <int D, int NW>
+template <int D, int NW, int TK = TILE>
 __device__ __forceinline__ uint32_t stage_lane_offset(int wave, int lane, bool is_v) {
-  using SG = StageGeom<D, NW>;
+  using SG = StageGeom<D, NW, TK>;
   const int r0 = wave * SG::RPI + lane / SG::CPR;
   return static_cast<uint32_t>(r0 * 2 * D + 16 * ((lane % SG::CPR) ^ (is_v ? v_swz<D>(r0) : k_swz<D>(r0))));
 }

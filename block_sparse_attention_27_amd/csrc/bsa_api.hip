@@ -8,8 +8,8 @@
 
 namespace {
 
-constexpr int kMaxSelectUnits = 4096;
-constexpr int kMaxClusterIters = 16;  // |valid units| * 2^20 must fit the 2^32 fixed point
+constexpr int kMaxSelectUnits = 4096;  // |valid units| * 2^20 must fit the 2^32 fixed point
+constexpr int kMaxClusterIters = 16;   // Lloyd iterations accepted by bsa_score_ibcs
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
