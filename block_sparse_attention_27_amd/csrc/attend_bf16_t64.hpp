@@ -149,6 +149,22 @@ __device__ __forceinline__ bool mask_tile64(f32x16 (&S)[2], const TileMeta& m, i
   return false;
 }
 
+// Largest shifted logit x + log2(w) of the 32 values a lane holds: sub-tile j
+// belongs to slot 32 j / S, whose log-weight it carries (c > 0, so the
+// maximum of the raw products scales to the maximum of x).
+template <int BK>
+__device__ __forceinline__ float tile_xmax64(const f32x16 (&S)[2], const TileMeta& m, float c) {
+  constexpr int SL = BK < T64 ? BK : T64;
+  float m0 = fmaxf(S[0][0], S[0][1]), m1 = fmaxf(S[1][0], S[1][1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) {
+    m0 = fmaxf(m0, fmaxf(S[0][r], S[0][r + 1]));
+    m1 = fmaxf(m1, fmaxf(S[1][r], S[1][r + 1]));
+  }
+  if constexpr (SL == 32) return fmaxf(fmaf(m0, c, m.lw[0]), fmaf(m1, c, m.lw[1]));
+  return fmaf(fmaxf(m0, m1), c, m.lw[0]);
+}
+
 template <int D, int BK, bool DENSE, bool PERM, bool OUT32>
 __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) {
   constexpr int NT = 64 * NW64;
@@ -241,15 +257,17 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // Running-max bookkeeping. When a tile's scores are complete, its maximum
-    // x decides the transition into it: rescale (need) when x exceeds the
-    // reference by more than the slack, to m_new, by alpha = 2^(m_ref - m_new).
-    // The transition is applied at the top of the step that computes the tile,
-    // after the previous tile's PV products have landed in O.
+    // Running-max bookkeeping on the shifted logits x + log2(w), so that no
+    // exponent exceeds 2^RESCALE_SLACK whatever the weights. When a tile's
+    // scores are complete, its maximum decides the transition into it:
+    // rescale (need) when it exceeds the reference by more than the slack, to
+    // m_new, by alpha = 2^(m_ref - m_new). The transition is applied at the top
+    // of the step that computes the tile, after the previous tile's PV
+    // products have landed in O.
     bool need = false;
     float m_new = m_ref, alpha = 1.f;
-    auto decide = [&](float mx_lane) {
-      const float mx = halves_max(mx_lane) * a.c;  // c > 0
+    auto decide = [&](float x_lane) {
+      const float mx = halves_max(x_lane);
       need = mx > m_ref + RESCALE_SLACK;
       m_new = need ? mx : m_ref;
       alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -257,7 +275,7 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
     f32x16 Sa[2], Sb[2];
     qk_tile<D>(Sa, K0, LO, qf);
     mask_tile64<BK>(Sa, meta0, h);
-    decide(tile_max(Sa));
+    decide(tile_xmax64<BK>(Sa, meta0, a.c));
 
     // One pipelined step: S_cur = QK(t) on entry, S_next = QK(t+1) on exit;
     // PAR = t & 1 selects the slots at compile time. mt and mt1 describe tiles
@@ -335,7 +353,7 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
 
       // ---- tiles with keys past a slot's end: mask S(t) and redo its maximum
       // (the previous step took it before masking); then the transition into t
-      if (mask_tile64<BK>(Scur, mt, h)) decide(tile_max(Scur));
+      if (mask_tile64<BK>(Scur, mt, h)) decide(tile_xmax64<BK>(Scur, mt, a.c));
       if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
@@ -384,7 +402,7 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
       // the two transposed reads of vread fetch e = 0..3 and 4..7. Alongside,
       // the maximum of S(t+1) (before masking, which the next step applies if
       // the tile needs it) and its transition decision.
-      float mx = -INFINITY;
+      float mx[2] = {-INFINITY, -INFINITY};  // per sub-tile: they may carry different weights
       constexpr int MS = NP - 3;
 #pragma unroll
       for (int m = 0; m < NP; ++m) {
@@ -395,11 +413,12 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
         if (m >= 2 && m < NP - 1) {
 #pragma unroll
           for (int q = (16 * (m - 2) + MS - 1) / MS; q < (16 * (m - 1) + MS - 1) / MS; ++q) {
-            mx = fmaxf(mx, fmaxf(Snext[q / 8][2 * (q % 8)], Snext[q / 8][2 * (q % 8) + 1]));
-            pin(mx);
+            mx[q / 8] = fmaxf(mx[q / 8], fmaxf(Snext[q / 8][2 * (q % 8)], Snext[q / 8][2 * (q % 8) + 1]));
+            pin(mx[q / 8]);
           }
         } else if (m == NP - 1) {
-          decide(mx);
+          if constexpr (SL == 32) decide(fmaxf(fmaf(mx[0], a.c, mt1.lw[0]), fmaf(mx[1], a.c, mt1.lw[1])));
+          else decide(fmaf(fmaxf(mx[0], mx[1]), a.c, mt1.lw[0]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(BQ) void attend_fp32_kernel(Fp32Args a) {
       float s = 0.f;
 #pragma unroll
       for (int col = 0; col < D; ++col) s = fmaf(qv[col], ks[r][col], s);
-      x[r] = r < cnt ? s * a.c : -INFINITY;
+      x[r] = r < cnt ? fmaf(s, a.c, lw) : -INFINITY;  // shifted logit x + log2(w)
       mx = fmaxf(mx, x[r]);
     }
     const float m_new = fmaxf(m, mx);
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(BQ) void attend_fp32_kernel(Fp32Args a) {
     m = m_new;
 #pragma unroll
     for (int r = 0; r < SEG; ++r) {
-      const float p = exp2f(x[r] - m + lw);
+      const float p = exp2f(x[r] - m);
       l += p;
 #pragma unroll
       for (int col = 0; col < D; ++col) acc[col] = fmaf(p, vs[r][col], acc[col]);

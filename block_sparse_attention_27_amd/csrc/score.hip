@@ -1,9 +1,9 @@
 // Block scoring for gfx950: block means of Q and K, then the estimated
 // attention mass of every key unit for every query block.
 //
-// What is computed (AB-Attention, Abstract: blocks scored from coarse block
-// summaries; InstaGen, Abstract: a sample drawn in proportion to estimated
-// attention):
+// What is computed (AB-Attention, Abstract: key blocks rated from cheap
+// per-block summaries; InstaGen, Abstract: the sampling chance of a block
+// follows its estimated share of attention):
 //   q_mean_i = mean of the valid rows of query block i  (0 if it has none)
 //   k_mean_j = mean of the n_j valid keys of unit j
 //   S_ij     = n_j exp(l_ij - L_i) / sum_{valid j'} n_j' exp(l_ij' - L_i),

@@ -2,12 +2,12 @@
 // sample weighted by inverse inclusion probability, one workgroup per
 // (b, h, query block).
 //
-// What is computed (InstaGen, Abstract: exact set computed in full, the rest
-// represented by a sample drawn in proportion to estimated attention and
-// reweighted by inverse sampling probability, one sample per query cluster;
-// AB-Attention transcript: inclusion probabilities with certain inclusion for
-// the strongest blocks, a fixed number of distinct blocks, probability 1/4 ->
-// weight 4):
+// What is computed (InstaGen, Abstract: the highest-scoring blocks are kept
+// whole, the others enter by a draw whose chance follows their estimated
+// attention and are scaled by one over that chance, with one draw per query
+// cluster; AB-Attention transcript: inclusion probabilities with certain
+// inclusion for the strongest blocks, a fixed number of distinct blocks,
+// probability 1/4 -> weight 4):
 //   1. exact set K = the k valid units with the largest score (ties: lower
 //      index; NaN/zero/negative scores count as 0, +inf as FLT_MAX);
 //   2. on the rest R, integer scores q_j = max(1, floor(s_j 2^(20 - e))) with

@@ -79,8 +79,13 @@ def _rel_err_per_head(o, ref, n_valid):
     return (num / den).flatten().tolist()
 
 
-def run_temperature(w, seeds, log=print):
-    """All estimators for one workload (one temperature). Returns a result dict."""
+def run_temperature(w, seeds, log=print, keep_lists=False):
+    """All estimators for one workload (one temperature). Returns a result dict.
+
+    With ``keep_lists`` the dict also holds, under "lists", every (estimator,
+    seed, problem, idx, w) that was fed to ``bsa_attend`` (host copies), so
+    that the numbers can be recomputed independently.
+    """
     import torch
 
     import block_sparse_attention_27_amd as bsa
@@ -98,8 +103,12 @@ def run_temperature(w, seeds, log=print):
     top = torch.topk(S, min(L, S.shape[-1]), dim=-1).values.sum(-1)
     top_mass = float(top.mean())
 
-    def err(p, idx, wt):
+    kept = []
+
+    def err(p, idx, wt, name=None, seed=None):
         o, lse = bsa.attend(p, q, k, v, idx, wt, perm, with_lse=True)
+        if keep_lists and name is not None:
+            kept.append((name, seed, bsa.Problem.from_buffer_copy(p), idx.cpu().numpy(), wt.cpu().numpy()))
         return statistics.mean(_rel_err_per_head(o, dense, w.N)), _d_ratio(lse, lse_d, w.N)
 
     res = {"workload": w.name, "values": w.value_mode, "temperature": w.temperature, "k_exact": w.k_exact,
@@ -111,7 +120,7 @@ def run_temperature(w, seeds, log=print):
 
     p_tr = bsa.problem_for(w, out_fp32=1, k_exact=L, m_sample=0)
     idx, wt = bsa.select(p_tr, S)
-    res["truncation"], res["truncation_dr"] = err(p_tr, idx, wt)
+    res["truncation"], res["truncation_dr"] = err(p_tr, idx, wt, "truncation")
     idx, wt = bsa.select(p_tr, S_ib)
     res["truncation_ibcs"], res["truncation_ibcs_dr"] = err(p_tr, idx, wt)
     idx, wt = bsa.select(p_tr, S_st)
@@ -121,11 +130,11 @@ def run_temperature(w, seeds, log=print):
     for s in seeds:
         p = bsa.problem_for(w, seed=s, out_fp32=1)
         idx, wt = bsa.select(p, S)
-        runs["weighted"].append(err(p, idx, wt))
-        runs["unweighted"].append(err(p, idx, torch.ones_like(wt)))
+        runs["weighted"].append(err(p, idx, wt, "weighted", s))
+        runs["unweighted"].append(err(p, idx, torch.ones_like(wt), "unweighted", s))
         p0 = bsa.problem_for(w, seed=s, out_fp32=1, k_exact=0, m_sample=L)
         idx0, wt0 = bsa.select(p0, S)
-        runs["sample_only"].append(err(p0, idx0, wt0))
+        runs["sample_only"].append(err(p0, idx0, wt0, "sample_only", s))
         idx, wt = bsa.select(p, S_ib)
         runs["weighted_ibcs"].append(err(p, idx, wt))
         idx, wt = bsa.select(p, S_st)
@@ -136,7 +145,10 @@ def run_temperature(w, seeds, log=print):
         res[name + "_std"] = statistics.pstdev(errs) if len(errs) > 1 else 0.0
         res[name + "_dr"] = statistics.mean(r for _, r in vals)
     torch.cuda.synchronize()
-    return {key: round(val, 5) if isinstance(val, float) else val for key, val in res.items()}
+    out = {key: round(val, 5) if isinstance(val, float) else val for key, val in res.items()}
+    if keep_lists:
+        out["lists"] = kept
+    return out
 
 
 def main(argv=None):

@@ -7,7 +7,7 @@
  * and the transcript's sections on inclusion-probability sampling and the
  * tiled kernel): every query block scores the key blocks from block summaries,
  * keeps the top-scoring ones as an exact set, draws a fixed-size sample of
- * the rest in proportion to the estimated attention, and runs one sparse
+ * the rest with chances that follow the estimated attention, and runs one sparse
  * attention pass in which every sampled block is reweighted by the inverse of
  * its inclusion probability in both the softmax numerator and denominator.
  *
@@ -95,8 +95,9 @@ const char* bsa_status_string(int32_t status);
 
 /*
  * bsa_score -- block summaries and estimated attention per key unit.
- * (AB-Attention, Abstract: blocks scored from coarse summaries; InstaGen,
- * Abstract: sample drawn in proportion to estimated attention.)
+ * (AB-Attention, Abstract: key blocks rated from cheap per-block summaries;
+ * InstaGen, Abstract: the sampling chance of a block follows its estimated
+ * share of attention.)
  *
  *   q_mean[b,h,i,:] = mean of the valid rows of query block i      (fp32, out)
  *   k_mean[b,h,j,:] = mean of the n_j valid keys of unit j          (fp32, out)
@@ -118,17 +119,28 @@ bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const i
  * from its size, and the representatives score the key blocks.)
  *
  * Per query block with n > 0 valid rows, Lloyd's k-means with `groups`
- * groups and `iters` iterations: initial centroid g = row floor(g n / groups)
- * of the block (after the optional gather); each iteration assigns every row
- * to its nearest centroid in squared Euclidean distance (ties: lower group)
- * and moves every centroid to the mean of its rows (an empty group keeps its
- * centroid). Then
+ * groups and `iters` iterations on fixed-point copies of the rows, so that
+ * every assignment is an exact integer decision:
+ *   q_int = rint(q 2^s) (nearest, ties to even), s = 11 - e, where the
+ *       block's largest |q| is f 2^e with f in [0.5, 1); |q_int| <= 2^11;
+ *   initial centroid g = q_int of row floor(g n / groups) of the block (after
+ *       the optional gather);
+ *   each iteration assigns every row to the centroid at the smallest exact
+ *       integer squared distance (ties: lower group), then moves every
+ *       non-empty group's centroid to floor((2 sum + n_g) / (2 n_g)), the
+ *       rounded mean of its rows' q_int (an empty group keeps its centroid).
+ * q_cent is the mean of the members' original values after the last
+ * assignment (fp32), and n_g the group's row count. Then
  *   S[b,h,i,j] = sum_g (n_g / n) n_j exp(l_gj) / sum_{valid j'} n_j' exp(l_gj'),
  *       l_gj = sm_scale <q_cent_ig, k_mean_j>;  S = 0 for invalid units.
+ * Group sizes are reproducible bit for bit. They equal those of plain fp64
+ * Lloyd k-means on the raw rows (same start, same iterations) whenever every
+ * assignment's distance margin exceeds the rounding bound
+ * 6 e sqrt(d D) + 9 e^2 d, e = 2^-(s+1); where the margins are smaller the two
+ * readings can group a row differently.
  * A query block with no valid row scores like bsa_score's (one zero
  * representative, weight 1) and reports zero centroids and sizes. With
- * groups = 1 the result is bsa_score's. Distances and sums are fp32, so a row
- * whose two nearest centroids are within fp32 rounding may join either.
+ * groups = 1 the result is bsa_score's.
  *   groups    1, 2, 4 or 8;  iters  1..16 (else BSA_ERR_INVALID_ARG)
  *   q_cent    [B][H][nQB][groups][d] fp32, out (16-byte aligned)
  *   q_size    [B][H][nQB][groups] int32, out: rows per group, n_g
@@ -190,11 +202,20 @@ bsa_status bsa_select(const bsa_problem* p, const float* S, int32_t* idx, float*
  *   out_r = sum_j w_j sum_t exp(a_rt) v_t / sum_j w_j sum_t exp(a_rt)
  *   lse_r = ln(sum_j w_j sum_t exp(a_rt))
  * The list is used as given (a repeated entry counts twice); entries with an
- * index outside [0, nKU) or a weight that is not > 0 contribute nothing.
+ * index outside [0, nKU) or a weight that is not a finite number > 0
+ * contribute nothing. Any finite positive weight is accepted (the running
+ * maximum of the online softmax is kept on the weighted logits, so no
+ * intermediate exceeds 2^8 times the largest weighted term).
  * idx/w may come from bsa_select or from the caller (e.g. a plan reused across
- * denoising steps). lse may be NULL. out is fp32 when out_fp32 is 1 or dtype
- * is BSA_FP32, else bf16; a bf16 out is the fp32 result rounded to nearest
- * even, bit for bit.
+ * denoising steps). lse may be NULL.
+ * Output type and accuracy: out is fp32 when out_fp32 is 1 or dtype is
+ * BSA_FP32, else bf16. For bf16 Q/K/V the fp32 output stays within 2e-3
+ * relative L2 of the exact (fp64) result on the layers this library is
+ * tested on (P is rounded to bf16 for the matrix cores: about 1.6e-3). A
+ * bf16 out is that fp32 result rounded to nearest even, bit for bit; the
+ * rounding adds about 1.7e-3 relative RMS of its own, so the bf16 output
+ * measures about 2.3e-3 relative L2 against the exact result (bounded by
+ * 2.5e-3 in the tests).
  */
 bsa_status bsa_attend(const bsa_problem* p, const void* q, const void* k, const void* v,
                       const int32_t* perm, const int32_t* idx, const float* w, void* out,
@@ -202,8 +223,12 @@ bsa_status bsa_attend(const bsa_problem* p, const void* q, const void* k, const 
 
 /*
  * bsa_attend_dense -- masked softmax(sm_scale Q K^T) V over the N valid keys,
- * same layouts, permutation and outputs as bsa_attend (k_exact, m_sample and
- * seed are ignored). The timing and accuracy reference for the sparse pass.
+ * same layouts, permutation, outputs and accuracy as bsa_attend (k_exact,
+ * m_sample and seed are ignored). It is full self-attention, the baseline the
+ * pages measure their sparse methods against (InstaGen, Abstract: speedup over
+ * the dense model; AB-Attention, Abstract: the share of attention skipped),
+ * and the limit the weighted pass reproduces when every valid unit is listed.
+ * The timing and accuracy reference for the sparse pass.
  */
 bsa_status bsa_attend_dense(const bsa_problem* p, const void* q, const void* k, const void* v,
                             const int32_t* perm, void* out, float* lse, hipStream_t stream);

@@ -29,7 +29,7 @@ rocRAND's host-callable Philox4x32-10).
 
 from .philox import philox4x32_10, philox4x32_10_np, block_offset
 from .scoring import apply_perm, unpermute, valid_counts, block_means, score
-from .ibcs import fixed_point, cluster_block, group_mixture, score_ibcs
+from .ibcs import fixed_point, cluster_block, lloyd_block, certified_agreement, group_mixture, score_ibcs
 from .stats_score import block_variances, score_stats
 from .selection import (sanitize, exact_set, quantise, water_fill, fixed_point_pi,
                         systematic_sample, inverse_weight, select_row, select, F_BITS, FS_BITS)
@@ -39,7 +39,7 @@ from .attention import (attend, attend_block, attend_dense, dense_block, dense_r
 __all__ = [
     "philox4x32_10", "philox4x32_10_np", "block_offset",
     "apply_perm", "unpermute", "valid_counts", "block_means", "score",
-    "fixed_point", "cluster_block", "group_mixture", "score_ibcs", "block_variances", "score_stats",
+    "fixed_point", "cluster_block", "lloyd_block", "certified_agreement", "group_mixture", "score_ibcs", "block_variances", "score_stats",
     "sanitize", "exact_set", "quantise", "water_fill", "fixed_point_pi",
     "systematic_sample", "inverse_weight", "select_row", "select", "F_BITS", "FS_BITS",
     "attend", "attend_block", "attend_dense", "dense_block", "dense_row_max",

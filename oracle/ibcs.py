@@ -40,6 +40,21 @@ readings taken here:
 
 With G = 1 the one representative is the block mean, so this is the plain
 scorer.
+
+The fixed-point width is set by exactness on the GPU's f16 matrix cores
+(every integer up to 2^11 is exact in f16, partial sums stay below 2^24).
+``lloyd_block`` is the unrounded reading -- plain Lloyd k-means in fp64 on
+the raw rows with the same initial rows, iteration count and tie rule -- and
+``certified_agreement`` states when the two must give the same groups: the
+rounding of rows (half a grid step e = 2^-(s+1) per coordinate) and of
+centroids (at most e more per coordinate against the mean of the rounded rows)
+moves a squared distance D over d dimensions by at most
+    6 e sqrt(d D) + 9 e^2 d   (centroids after an update),
+    4 e sqrt(d D) + 4 e^2 d   (initial centroids, themselves rounded rows),
+so an assignment whose plain-Lloyd margin over every other group exceeds the
+sum of the two groups' bounds is taken identically; when every assignment of
+every iteration clears that margin, both readings hold the same members
+throughout and return the same sizes and representatives.
 """
 
 from __future__ import annotations
@@ -90,6 +105,62 @@ def cluster_block(rows: np.ndarray, groups: int, iters: int, history: bool = Fal
     if history:
         return reps, sizes, hist, qi
     return reps, sizes
+
+
+def lloyd_block(rows: np.ndarray, groups: int, iters: int, history: bool = False):
+    """Plain Lloyd k-means of one block's rows in fp64, no rounding.
+
+    Initial centroid g is row floor(g n / G); each iteration assigns every row
+    to its nearest centroid in squared Euclidean distance (ties: the lower
+    group) and moves every non-empty group's centroid to the mean of its rows.
+    Returns (representatives [G, d], sizes [G]) like ``cluster_block``; with
+    ``history`` also, per iteration, the [n, G] squared distances that decided
+    the assignment and the centroids they were measured against.
+    """
+    rows = np.asarray(rows, dtype=np.float64)
+    n = rows.shape[0]
+    c = rows[[(g * n) // groups for g in range(groups)]].copy()
+    lab = np.zeros(n, dtype=np.int64)
+    hist = []
+    for _ in range(iters):
+        d2 = ((rows[:, None, :] - c[None, :, :]) ** 2).sum(axis=-1)
+        hist.append((d2, c.copy()))
+        lab = np.argmin(d2, axis=1)
+        for g in range(groups):
+            if (lab == g).any():
+                c[g] = rows[lab == g].mean(axis=0)
+    sizes = np.bincount(lab, minlength=groups).astype(np.int64)
+    reps = np.zeros((groups, rows.shape[1]))
+    for g in range(groups):
+        if sizes[g]:
+            reps[g] = rows[lab == g].sum(axis=0) / sizes[g]
+    if history:
+        return reps, sizes, hist
+    return reps, sizes
+
+
+def certified_agreement(rows: np.ndarray, groups: int, iters: int) -> bool:
+    """True when every plain-Lloyd assignment clears the rounding bound of the
+    fixed-point reading in every iteration (see the module notes), so that
+    ``cluster_block`` and ``lloyd_block`` must agree on this block."""
+    rows = np.asarray(rows, dtype=np.float64)
+    _, s = fixed_point(rows)
+    e = math.ldexp(0.5, -s)
+    d = rows.shape[1]
+    _, _, hist = lloyd_block(rows, groups, iters, history=True)
+    for it, (d2, _) in enumerate(hist):
+        a, b = (4.0, 4.0) if it == 0 else (6.0, 9.0)
+        bound = a * e * np.sqrt(d * d2) + b * e * e * d
+        bound *= 1 + 1e-9  # fp64 evaluation of the distances themselves
+        best = np.argmin(d2, axis=1)
+        r = np.arange(d2.shape[0])
+        gap = d2 - d2[r, best][:, None]
+        need = bound + bound[r, best][:, None]
+        other = np.ones_like(d2, dtype=bool)
+        other[r, best] = False
+        if np.any(other & (gap <= need)):
+            return False
+    return True
 
 
 def group_mixture(cent: np.ndarray, weights: np.ndarray, k_bar: np.ndarray, n_j: np.ndarray,

@@ -2,9 +2,9 @@
 
 Test infrastructure: part of the CPU oracle (see ``oracle/__init__.py``).
 
-What it computes (AB-Attention, Abstract: blocks are scored from coarse block
-summaries; InstaGen, Abstract: the sample is drawn in proportion to estimated
-attention):
+What it computes (AB-Attention, Abstract: key blocks are rated from cheap
+per-block summaries; InstaGen, Abstract: the sampling chance of a block follows
+its estimated share of attention):
 
 * q_bar[i] = mean of the valid rows of query block i (rows r < N of the
   permuted sequence); a block with no valid row gets the zero vector;

@@ -4,10 +4,10 @@ Test infrastructure: part of the CPU oracle (see ``oracle/__init__.py``).
 
 What the pages fix:
 
-* the top-scoring key blocks form an exact set that is computed in full; the
-  remaining blocks are represented by a sample drawn in proportion to their
-  estimated attention and reweighted by the inverse of the sampling
-  probability (InstaGen, Abstract; AB-Attention, Abstract);
+* each query block attends exactly to its highest-scoring key blocks; every
+  other block can enter only through a random draw whose chance grows with the
+  block's estimated attention, and a drawn block is scaled up by one over that
+  chance (InstaGen, Abstract; AB-Attention, Abstract);
 * scores set per-block inclusion probabilities, the most important blocks can
   be taken with certainty while every other block keeps a nonzero chance, and
   the sampler returns a fixed number of distinct blocks so the budget is

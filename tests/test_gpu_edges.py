@@ -231,10 +231,39 @@ def test_scores_more_units_than_the_logit_cache(d, bq, dtype, perm):
     assert rel_l2(qm.cpu().numpy(), qb) < 1e-5 and rel_l2(km.cpu().numpy(), kb) < 1e-5
 
 
+@pytest.mark.parametrize("bq,dtype", [(128, "bf16"), (64, "bf16"), (128, "fp32")])
+def test_extreme_weights(bq, dtype):
+    # caller-built lists with weights from 2^-100 to FLT_MAX: the running maximum is kept on the
+    # weighted logits, so nothing overflows and the result is the oracle's (fp64) weighted softmax
+    print_case(f"extreme weights: bq={bq} {dtype}")
+    w = _small(128, bq, 64, dtype, False, k=2, m=6, seed=3)
+    g = generate(w)
+    q, k, v = (to_device(g[x]) for x in ("q", "k", "v"))
+    p = bsa.problem_for(w, out_fp32=1)
+    rng = np.random.default_rng(13)
+    shape = (w.B, w.H, w.n_qblocks, w.list_len)
+    idx = rng.integers(0, w.n_valid_units, shape).astype(np.int32)
+    wts = np.exp2(rng.uniform(-100, 100, shape)).astype(np.float32)
+    wts[:, :, ::3, 0] = np.finfo(np.float32).max
+    wts[:, :, 1::3, 1] = np.finfo(np.float32).tiny
+    out, lse = bsa.attend(p, q, k, v, torch.from_numpy(idx).cuda(), torch.from_numpy(wts).cuda(), with_lse=True)
+    torch.cuda.synchronize()
+    qh, kh, vh = (host_f64(g[x]) for x in ("q", "k", "v"))
+    O_ref, L_ref = oracle.attend(qh, kh, vh, w.N, w.block_q, w.block_k, w.sm_scale, idx, wts)
+    got = to_f64(out)
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, O_ref) <= 2e-3 and np.max(np.abs(got - O_ref)) <= 1e-2
+    lg = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(L_ref)
+    assert np.array_equal(np.isfinite(lg), fin)
+    assert np.max(np.abs(lg[fin] - L_ref[fin]) / np.maximum(1.0, np.abs(L_ref[fin]))) < 2e-3
+
+
 @pytest.mark.parametrize("perm", [False, True])
 def test_lists_longer_than_one_chunk(perm):
-    # 1,100 list entries per query block: the attention kernel takes them in two sorted chunks
-    # of at most 1,024 entries (with a permutation, the gathered-row ring restarts per chunk)
+    # 1,100 list entries per query block: the attention kernel takes them in sorted chunks (of at
+    # most 512 entries for 128-row query blocks; with a permutation, the gathered-row ring restarts
+    # per chunk)
     print_case(f"lists of 1100 entries (two chunks), permuted={perm}")
     w = Workload("long", B=1, H=1, grid=(12, 50, 80), d=128, dtype="bf16", block_q=128, block_k=32,
                  k_exact=100, m_sample=1000, clusters=16, temperature=1.0, permute=perm, seed=9, select_seed=4)

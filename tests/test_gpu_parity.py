@@ -6,8 +6,10 @@ Bars (written here, applied per check):
   attention  relative L2 <= 2e-3 and max |diff| <= 1e-2 over the checked rows,
              fed the same idx/w, on the fp32 output of the bf16 MFMA path;
              lse within 2e-3 absolute; the bf16 output is bit-identical to
-             the fp32 output rounded to nearest even (its only extra error
-             is its own rounding, ~1.7e-3 relative L2 on these workloads).
+             the fp32 output rounded to nearest even, and within 2.5e-3
+             relative L2 (1e-2 max-abs) of the oracle: its own rounding adds
+             ~1.7e-3 relative RMS to the fp32 output's ~1.6e-3, about 2.3e-3
+             in all.
 Small workloads are compared whole; the full-size layers are compared on
 sampled (head, query block) pairs that include the first and the padded last
 block, in the launch configuration the bench times.
@@ -29,6 +31,7 @@ pytestmark = pytest.mark.gpu
 SCORE_RTOL = 1e-3
 OUT_REL_L2 = 2e-3
 OUT_MAX_ABS = 1e-2
+OUT16_REL_L2 = 2.5e-3
 LSE_ABS = 2e-3
 
 
@@ -85,7 +88,7 @@ def check_bf16_is_rounded_fp32(out_bf16, out_f32):
 
 
 def run_attend(p, dev, idx, wt, dense=False):
-    """bf16-output and fp32-output runs of the same call; returns (out_f32, lse) after the bit check."""
+    """bf16-output and fp32-output runs of the same call; returns (out_f32, lse, out_bf16) after the bit check."""
     p32 = bsa.Problem.from_buffer_copy(p)
     p32.out_fp32 = 1
     if dense:
@@ -96,14 +99,14 @@ def run_attend(p, dev, idx, wt, dense=False):
         o32, lse = bsa.attend(p32, dev["q"], dev["k"], dev["v"], idx, wt, dev["perm"], with_lse=True)
     torch.cuda.synchronize()
     check_bf16_is_rounded_fp32(o16, o32)
-    del o16
-    return o32, lse
+    return o32, lse, o16
 
 
-def check_attention(w, g, out_gpu, lse_gpu, idx, wt, pairs, dense=False):
+def check_attention(w, g, out_gpu, lse_gpu, idx, wt, pairs, dense=False, out16=None):
     perm = g["perm"]
     out = out_gpu
     errs = []
+    errs16 = []
     for h, blocks in pairs.items():
         q = host_f64(_head(g["q"], h)); k = host_f64(_head(g["k"], h)); v = host_f64(_head(g["v"], h))
         tri = [(0, 0, i) for i in blocks]
@@ -117,6 +120,8 @@ def check_attention(w, g, out_gpu, lse_gpu, idx, wt, pairs, dense=False):
             orows = np.where(rows < w.N, perm[rows] if perm is not None else rows, rows)
             got = to_f64(out[0, h, torch.from_numpy(orows).cuda()])
             errs.append((got, o_ref))
+            if out16 is not None:
+                errs16.append(to_f64(out16[0, h, torch.from_numpy(orows).cuda()]))
             if lse_gpu is not None:
                 gl = lse_gpu[0, h, torch.from_numpy(orows).cuda()].cpu().numpy().astype(np.float64)
                 ok = rows < w.N
@@ -127,6 +132,11 @@ def check_attention(w, g, out_gpu, lse_gpu, idx, wt, pairs, dense=False):
     r, m = rel_l2(got, ref), float(np.max(np.abs(got - ref)))
     print_case(f"  rel_l2={r:.3e} max_abs={m:.3e}")
     assert r <= OUT_REL_L2 and m <= OUT_MAX_ABS, (r, m)
+    if out16 is not None:
+        got16 = np.concatenate(errs16)
+        r16, m16 = rel_l2(got16, ref), float(np.max(np.abs(got16 - ref)))
+        print_case(f"  bf16 output: rel_l2={r16:.3e} max_abs={m16:.3e}")
+        assert r16 <= OUT16_REL_L2 and m16 <= OUT_MAX_ABS, (r16, m16)
 
 
 # ------------------------------------------------------------------ tiny (fp32)
@@ -176,7 +186,7 @@ def test_layer_score_select_attend(name):
     S, qm, km = bsa.score(p, dev["q"], dev["k"], dev["perm"])
     idx, wt = bsa.select(p, S)
     torch.cuda.synchronize()
-    out, lse = run_attend(p, dev, idx, wt)
+    out, lse, out16 = run_attend(p, dev, idx, wt)
 
     print_case(f"{name}: scores vs oracle")
     check_scores(w, g, S, list(range(n_s_heads)))
@@ -190,8 +200,8 @@ def test_layer_score_select_attend(name):
     print_case(f"{name}: attention vs oracle with the same lists")
     heads, blocks = _sample_blocks(w, n_a_heads, n_a_blocks)
     idx_h, wt_h = idx.cpu().numpy(), wt.cpu().numpy()
-    check_attention(w, g, out, lse, idx_h, wt_h, {h: blocks for h in heads})
-    del out, lse
+    check_attention(w, g, out, lse, idx_h, wt_h, {h: blocks for h in heads}, out16=out16)
+    del out, lse, out16
 
 
 @pytest.mark.parametrize("name", ["wan13b", "hunyuan"])
@@ -199,9 +209,9 @@ def test_layer_dense(name):
     print_case(f"{name}: bsa_attend_dense vs oracle")
     w, g, dev = workload_data(name)
     p = bsa.problem_for(w)
-    out, lse = run_attend(p, dev, None, None, dense=True)
+    out, lse, out16 = run_attend(p, dev, None, None, dense=True)
     heads, blocks = _sample_blocks(w, 1, 3, seed=2)
-    check_attention(w, g, out, lse, None, None, {h: blocks for h in heads}, dense=True)
+    check_attention(w, g, out, lse, None, None, {h: blocks for h in heads}, dense=True, out16=out16)
 
 
 def test_480p_temperature_sweep_selection_and_scores():
@@ -214,8 +224,8 @@ def test_480p_temperature_sweep_selection_and_scores():
         p = bsa.problem_for(w)
         S, _, _ = bsa.score(p, q, k)
         idx, wt = bsa.select(p, S)
-        out, _ = run_attend(p, {"q": q, "k": k, "v": v, "perm": None}, idx, wt)
+        out, _, out16 = run_attend(p, {"q": q, "k": k, "v": v, "perm": None}, idx, wt)
         check_scores(w, g, S, [0, 3])
         rows = [(0, h, i) for h in range(4) for i in range(0, w.n_qblocks, 7)]
         check_selection(w, S, idx, wt, rows, w.select_seed)
-        check_attention(w, g, out, None, idx.cpu().numpy(), wt.cpu().numpy(), {1: [0, 100, 255]})
+        check_attention(w, g, out, None, idx.cpu().numpy(), wt.cpu().numpy(), {1: [0, 100, 255]}, out16=out16)

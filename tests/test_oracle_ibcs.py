@@ -1,15 +1,17 @@
 """Pins for the oracle's intra-block clustering scorer (CPU only): the one-group
 case against the plain scorer, exact two-cluster blocks against a direct
 softmax mixture, tie and empty-group handling worked by hand, the fixed-point
-rounding rule, Lloyd iterations against scikit-learn's KMeans, the k-means
-cost bound of rounded centroids, and the invariants of the full score matrix."""
+rounding rule, plain fp64 Lloyd on raw rows against scikit-learn's KMeans, the
+fixed-point reading against both wherever every assignment clears the derived
+rounding margin, the k-means cost bound of rounded centroids, and the
+invariants of the full score matrix."""
 
 import numpy as np
 import pytest
 from scipy.special import softmax
 
 from oracle import score, valid_counts
-from oracle.ibcs import cluster_block, fixed_point, group_mixture, score_ibcs
+from oracle.ibcs import certified_agreement, cluster_block, fixed_point, group_mixture, lloyd_block, score_ibcs
 
 
 def _tiny(seed=0, B=1, H=2, N=300, N_pad=384, d=16):
@@ -103,22 +105,81 @@ def test_fewer_rows_than_groups():
     assert np.array_equal(reps, np.array([rows[0], [0.0, 0.0], rows[1], rows[2]]))
 
 
-def test_lloyd_iterations_match_scikit_learn():
+def _separated(rng, groups, d=16, n=128, spread=3.0):
+    """n rows around ``groups`` centres in contiguous runs, so the initial rows floor(g n / G) start
+    in different clusters; unit Gaussian noise."""
+    centres = rng.standard_normal((groups, d)) * spread
+    return centres[(np.arange(n) * groups) // n] + rng.standard_normal((n, d))
+
+
+LLOYD_CASES = ((4, 1), (4, 2), (4, 5), (2, 3), (8, 4), (3, 6))
+
+
+def test_plain_lloyd_matches_scikit_learn_on_raw_rows():
+    # the unrounded reading (plain fp64 Lloyd on the raw rows) against a library k-means
     KMeans = pytest.importorskip("sklearn.cluster").KMeans
-    for groups, iters in ((4, 1), (4, 2), (4, 5), (2, 3), (8, 4), (3, 6)):
+    for groups, iters in LLOYD_CASES:
         rng = np.random.default_rng(100 + 10 * groups + iters)
-        centres = rng.standard_normal((groups, 16)) * 2
-        rows = centres[rng.integers(0, groups, 128)] + rng.standard_normal((128, 16))
-        qi, s = fixed_point(rows)
-        rows = np.ldexp(qi.astype(np.float64), -s)  # on the fixed-point grid: the same points for both
-        reps, sizes = cluster_block(rows, groups, iters)
+        rows = _separated(rng, groups, spread=2.0)
+        reps, sizes = lloyd_block(rows, groups, iters)
         assert sizes.min() > 0  # scikit-learn relocates empty clusters; keep them out of the comparison
         init = rows[[(g * 128) // groups for g in range(groups)]]
         km = KMeans(n_clusters=groups, init=init, n_init=1, max_iter=iters, tol=0.0,
                     algorithm="lloyd").fit(rows)
-        # scikit-learn's centres are the means of its last assignment, as the representatives
-        # are; the rounded fixed-point centroids move no assignment on these rows
+        # scikit-learn's centres are the means of its last assignment, as the representatives are
         assert np.allclose(reps, km.cluster_centers_, rtol=1e-9, atol=1e-9), (groups, iters)
+
+
+def test_fixed_point_reading_matches_scikit_learn_on_certified_raw_rows():
+    # the kernel's reading (rows and centroids on the 2^(e-11) grid) on raw, unsnapped rows: where every
+    # assignment clears the derived rounding margin, its groups are scikit-learn's Lloyd groups
+    KMeans = pytest.importorskip("sklearn.cluster").KMeans
+    checked = 0
+    for groups, iters in LLOYD_CASES:
+        for seed in range(4):
+            rng = np.random.default_rng(1000 * seed + 10 * groups + iters)
+            rows = _separated(rng, groups)
+            if not certified_agreement(rows, groups, iters):
+                continue
+            reps, sizes = cluster_block(rows, groups, iters)
+            if sizes.min() == 0:
+                continue
+            init = rows[[(g * 128) // groups for g in range(groups)]]
+            km = KMeans(n_clusters=groups, init=init, n_init=1, max_iter=iters, tol=0.0,
+                        algorithm="lloyd").fit(rows)
+            assert np.allclose(reps, km.cluster_centers_, rtol=1e-9, atol=1e-9), (groups, iters, seed)
+            checked += 1
+    assert checked >= 12, checked
+
+
+def test_fixed_point_reading_equals_plain_lloyd_when_certified():
+    # certified blocks: identical sizes and bit-identical representatives (same members, same sums)
+    certified = 0
+    for case in range(60):
+        rng = np.random.default_rng(5000 + case)
+        groups = (2, 4, 8)[case % 3]
+        iters = (1, 3, 5)[(case // 3) % 3]
+        spread = (3.0, 4.0, 6.0, 8.0)[(case // 9) % 4]
+        d = (16, 64, 128)[case % 3]
+        rows = _separated(rng, groups, d=d, n=(128, 97, 64)[case % 3], spread=spread)
+        rows *= 10.0 ** rng.uniform(-3, 3)  # the grid follows the block's own magnitude
+        if not certified_agreement(rows, groups, iters):
+            continue
+        certified += 1
+        r1, s1 = cluster_block(rows, groups, iters)
+        r2, s2 = lloyd_block(rows, groups, iters)
+        assert np.array_equal(s1, s2), case
+        assert np.array_equal(r1, r2), case
+    assert certified >= 30, certified
+
+
+def test_certification_bound_is_not_vacuous():
+    # two rows a grid step apart from a third, with the centroid rounding able to swap them: the rule
+    # must refuse to certify a block whose margins are below the rounding scale
+    rows = np.array([[1.0, 0.0], [1.0 + 2.0 ** -12, 0.0], [1.0 + 2.0 ** -11, 0.0], [-1.0, 0.0]])
+    assert not certified_agreement(rows, 2, 2)
+    far = np.array([[1.0, 0.0], [1.01, 0.0], [-1.0, 0.0], [-1.01, 0.0]])
+    assert certified_agreement(far, 2, 3)
 
 
 def test_kmeans_cost_bound_with_rounded_centroids():
