@@ -27,7 +27,10 @@
 // Layout: thread t owns the E consecutive units [t E, t E + E), so exclusive
 // scans give ranks in unit order directly. Rows of up to 1024 valid units take
 // one wave each (ballot counts, DPP sums and scans, no barriers); longer rows take a
-// 256-thread workgroup.
+// 256-thread workgroup. The threshold of the exact set is found bit by bit,
+// most significant first: the top 12 bits over every key, the low 19 over the
+// few keys that share the threshold's top bits, gathered into LDS (one wave
+// finishes them without barriers).
 #include "bsa_internal.hpp"
 
 namespace bsa {
@@ -150,55 +153,83 @@ __device__ __forceinline__ uint64_t wave_inclusive_scan(uint64_t x) {
   return x;
 }
 
+// Workgroup reductions with one barrier each: every reduction writes the
+// half of its buffer given by a parity that flips at every reduction, so a
+// half is rewritten only after the next reduction's barrier, which every
+// thread reaches after its reads of this one.
+struct BlockRed {
+  uint64_t r64[2][SEL_WAVES];
+  uint32_t r32[2][SEL_WAVES];
+};
+
 template <typename T>
-__device__ __forceinline__ T block_sum(T v, T* red) {
+__device__ __forceinline__ T* red_half(BlockRed& r, int par) {
+  if constexpr (sizeof(T) == 8) return r.r64[par];
+  else return r.r32[par];
+}
+
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, BlockRed& r, int& par) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  T* red = red_half<T>(r, par);
+  par ^= 1;
   v = wave_sum(v);
   if (lane == 0) red[wave] = v;
   __syncthreads();
   T t = 0;
 #pragma unroll
   for (int x = 0; x < SEL_WAVES; ++x) t += red[x];
-  __syncthreads();
   return t;
 }
 
-__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
+__device__ __forceinline__ uint32_t block_max(uint32_t v, BlockRed& r, int& par) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  uint32_t* red = r.r32[par];
+  par ^= 1;
   v = wave_max_u32(v);
   if (lane == 0) red[wave] = v;
   __syncthreads();
   uint32_t t = 0;
 #pragma unroll
   for (int x = 0; x < SEL_WAVES; ++x) t = max(t, red[x]);
-  __syncthreads();
   return t;
 }
 
 // Exclusive prefix over threads in index order; `total` receives the block sum.
-__device__ __forceinline__ uint64_t block_exscan(uint64_t v, uint64_t* red, uint64_t& total) {
+__device__ __forceinline__ uint64_t block_exscan(uint64_t v, BlockRed& r, int& par, uint64_t& total) {
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  uint64_t* red = r.r64[par];
+  par ^= 1;
   const uint64_t x = wave_inclusive_scan(v);
   if (lane == 63) red[wave] = x;
   __syncthreads();
   uint64_t before = 0, tot = 0;
 #pragma unroll
   for (int z = 0; z < SEL_WAVES; ++z) {
-    const uint64_t r = red[z];
-    if (z < wave) before += r;
-    tot += r;
+    const uint64_t rz = red[z];
+    if (z < wave) before += rz;
+    tot += rz;
   }
-  __syncthreads();
   total = tot;
   return before + x - v;
 }
 
+// The threshold search of the exact set runs in two phases: the top bits
+// 30..SPLIT over every key, then the low SPLIT bits over the keys that share
+// the threshold's top bits ("in play"), compacted into LDS. For the largest
+// prefix P with at least k keys >= P, fewer than k keys lie above P's bin, so
+// the low bits are the search for the (k - above)-th largest in-play key.
+constexpr int SPLIT = 19;      // top 12 bits: the exponent and 4 mantissa bits
+constexpr int PLAY_MAX = 256;  // in-play keys one wave finishes (4 per lane); more take the block loop
+
 template <int E>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
+  static_assert(PLAY_MAX <= SEL_THREADS * E, "the in-play keys borrow the row's staging array");
   __shared__ uint32_t sbits[SEL_THREADS * E];
-  __shared__ uint64_t red64[SEL_WAVES];
-  __shared__ uint32_t red32[SEL_WAVES];
+  __shared__ BlockRed red;
   __shared__ uint32_t cnt2[2][SEL_WAVES];  // per-wave counts, alternating buffers
+  __shared__ uint32_t t_bcast;
+  int par = 0;  // reduction buffer half (uniform)
 
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -222,82 +253,124 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   }
   __syncthreads();
 
+  // Per-unit state stays small (three waves per SIMD at 135 registers was
+  // the limit before): validity is recomputed from the unit index, the exact
+  // set and the capped units are bit masks (bit e: unit tid E + e), and pi
+  // (1 <= pi <= 2^32 on R) is held as pi - 1 in 32 bits.
+  const int j0 = tid * E;
+  auto valid = [&](int e) { return j0 + e < a.nV; };
   uint32_t key[E];
-  bool valid[E], inK[E];
+  uint32_t fK = 0, fcap = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = tid * E + e;
-    valid[e] = j < a.nV;
-    key[e] = valid[e] ? sanitize(sbits[j]) : 0u;
-    inK[e] = false;
-  }
+  for (int e = 0; e < E; ++e) key[e] = valid(e) ? sanitize(sbits[j0 + e]) : 0u;
 
   // ---- 1. exact set: T = k-th largest key, ties by lower index ----
   if (a.k > 0) {
     // counts from ballots (cand >= 1 and invalid units hold key 0); one
     // barrier per bit: a buffer is rewritten two bits later, after every
     // thread has passed the barrier that follows its reads
-    const int wave = tid / 64;
+    const int wave = tid / 64, lane = tid % 64;
     uint32_t T = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      uint32_t c = 0;
+    auto block_bits = [&](int top, int low) {
+      for (int bit = top; bit >= low; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        uint32_t c = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
-      if (tid % 64 == 0) cnt2[bit & 1][wave] = c;
+        for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
+        if (lane == 0) cnt2[bit & 1][wave] = c;
+        __syncthreads();
+        uint32_t tot = 0;
+#pragma unroll
+        for (int x = 0; x < SEL_WAVES; ++x) tot += cnt2[bit & 1][x];
+        if (tot >= static_cast<uint32_t>(a.k)) T = cand;
+      }
+    };
+    block_bits(30, SPLIT);
+    // keys above T's bin, and the keys in it (hi may be 2^31: no key reaches it)
+    const uint32_t hi = T + (1u << SPLIT);
+    uint32_t n_above = 0, n_play = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      n_above += (valid(e) && key[e] >= hi) ? 1u : 0u;
+      n_play += (valid(e) && key[e] >= T && key[e] < hi) ? 1u : 0u;
+    }
+    uint64_t tot;
+    const uint64_t pos = block_exscan((static_cast<uint64_t>(n_above) << 32) | n_play, red, par, tot);
+    const uint32_t above = static_cast<uint32_t>(tot >> 32), play = static_cast<uint32_t>(tot);
+    if (play <= static_cast<uint32_t>(PLAY_MAX)) {
+      // every key is in registers and the exscan's barrier has passed: the
+      // staging array takes the in-play keys
+      uint32_t p = static_cast<uint32_t>(pos);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (valid(e) && key[e] >= T && key[e] < hi) sbits[p++] = key[e];
       __syncthreads();
-      uint32_t tot = 0;
+      if (wave == 0) {
+        const uint32_t need = static_cast<uint32_t>(a.k) - above;  // >= 1
+        uint32_t ck[PLAY_MAX / 64];
 #pragma unroll
-      for (int x = 0; x < SEL_WAVES; ++x) tot += cnt2[bit & 1][x];
-      if (tot >= static_cast<uint32_t>(a.k)) T = cand;
+        for (int z = 0; z < PLAY_MAX / 64; ++z) {
+          const uint32_t x = static_cast<uint32_t>(lane + 64 * z);
+          ck[z] = x < play ? sbits[x] : 0u;  // padding 0 never reaches cand >= 1
+        }
+        for (int bit = SPLIT - 1; bit >= 0; --bit) {
+          const uint32_t cand = T | (1u << bit);
+          uint32_t c = 0;
+#pragma unroll
+          for (int z = 0; z < PLAY_MAX / 64; ++z) c += __popcll(__ballot(ck[z] >= cand));
+          if (c >= need) T = cand;
+        }
+        if (lane == 0) t_bcast = T;
+      }
+      __syncthreads();
+      T = t_bcast;
+    } else {
+      block_bits(SPLIT - 1, 0);
     }
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      gt += (valid[e] && key[e] > T) ? 1u : 0u;
-      eq += (valid[e] && key[e] == T) ? 1u : 0u;
+      gt += (valid(e) && key[e] > T) ? 1u : 0u;
+      eq += (valid(e) && key[e] == T) ? 1u : 0u;
     }
-    const uint32_t need = static_cast<uint32_t>(a.k) - block_sum(gt, red32);
-    uint64_t eq_total;
-    uint32_t r = static_cast<uint32_t>(block_exscan(eq, red64, eq_total));
+    // one scan: the count above T (high word, total only) and the ranks of the keys equal to T
+    uint64_t ge_total;
+    const uint64_t ge = block_exscan((static_cast<uint64_t>(gt) << 32) | eq, red, par, ge_total);
+    const uint32_t need = static_cast<uint32_t>(a.k) - static_cast<uint32_t>(ge_total >> 32);
+    uint32_t r = static_cast<uint32_t>(ge);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (!valid[e]) continue;
+      if (!valid(e)) continue;
       if (key[e] > T) {
-        inK[e] = true;
+        fK |= 1u << e;
       } else if (key[e] == T) {
-        inK[e] = r < need;
+        if (r < need) fK |= 1u << e;
         ++r;
       }
     }
   }
+  auto inK = [&](int e) { return ((fK >> e) & 1u) != 0u; };
+  auto inR = [&](int e) { return valid(e) && !inK(e); };
+  auto capped = [&](int e) { return ((fcap >> e) & 1u) != 0u; };
 
-  bool inR[E], capped[E];
-  uint64_t pi[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    inR[e] = valid[e] && !inK[e];
-    capped[e] = false;
-    pi[e] = 0;
-  }
-
+  uint32_t pim1[E];  // pi - 1 on R (pi in [1, 2^32])
   uint64_t delta = 0;
   if (a.m > 0) {
     // ---- 2a. quantised scores over R ----
     uint32_t mx = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (inR[e]) mx = max(mx, key[e]);
-    mx = block_max(mx, red32);
+      if (inR(e)) mx = max(mx, key[e]);
+    mx = block_max(mx, red, par);
     uint32_t q[E];
     const int ex = mx ? frexp_exp(mx) : 0;
     uint64_t qsum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      q[e] = inR[e] ? (mx ? quantise(key[e], ex) : 1u) : 0u;
+      q[e] = inR(e) ? (mx ? quantise(key[e], ex) : 1u) : 0u;
       qsum += q[e];
     }
-    uint64_t QU = block_sum(qsum, red64);
+    uint64_t QU = block_sum(qsum, red, par);
 
     // ---- 2b. water-filling on exact integers ----
     uint64_t t = 0;
@@ -306,12 +379,12 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
       uint64_t packed = 0;  // (count << 40) | sum of q
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        if (inR[e] && !capped[e] && mt * q[e] >= QU) {
-          capped[e] = true;
+        if (inR(e) && !capped(e) && mt * q[e] >= QU) {
+          fcap |= 1u << e;
           packed += (1ull << 40) + q[e];
         }
       }
-      packed = block_sum(packed, red64);
+      packed = block_sum(packed, red, par);
       const uint64_t cnt = packed >> 40;
       if (cnt == 0) break;
       t += cnt;
@@ -321,46 +394,45 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
     // ---- 2c. fixed-point pi ----
     // (m - t) q_j < 2^33 and Q_U < 2^33 are exact in fp64, and so is their
     // product form below; an uncapped unit has (m - t) q_j < Q_U, so its
-    // correctly rounded ratio is below 1 and 2^32 ratio fits 32 bits.
+    // correctly rounded ratio is below 1 and 2^32 ratio fits 32 bits (>= 1).
     const uint64_t mt = static_cast<uint64_t>(a.m) - t;
     const double mt_d = static_cast<double>(static_cast<uint32_t>(mt));
     const double qu_d = static_cast<double>(QU);
     uint64_t usum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (!inR[e]) continue;
-      if (capped[e]) {
-        pi[e] = 1ull << 32;
-      } else {
+      pim1[e] = 0xFFFFFFFFu;  // capped: pi = 2^32
+      if (inR(e) && !capped(e)) {
         const double ratio = (mt_d * static_cast<double>(q[e])) / qu_d;
-        pi[e] = static_cast<uint32_t>(ratio * 4294967296.0);
-        usum += pi[e];
+        const uint32_t pv = static_cast<uint32_t>(ratio * 4294967296.0);
+        pim1[e] = pv - 1u;
+        usum += pv;
       }
     }
-    delta = (mt << 32) - block_sum(usum, red64);
+    delta = (mt << 32) - block_sum(usum, red, par);
   }
 
   // ---- ranks in unit order: K (high word) and uncapped R (low word) ----
   uint32_t nk = 0, nu = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    nk += inK[e] ? 1u : 0u;
-    nu += (inR[e] && !capped[e]) ? 1u : 0u;
+    nk += inK(e) ? 1u : 0u;
+    nu += (inR(e) && !capped(e)) ? 1u : 0u;
   }
   uint64_t rk_total;
-  const uint64_t rk = block_exscan((static_cast<uint64_t>(nk) << 32) | nu, red64, rk_total);
+  const uint64_t rk = block_exscan((static_cast<uint64_t>(nk) << 32) | nu, red, par, rk_total);
   uint32_t kpos = static_cast<uint32_t>(rk >> 32);
   uint32_t upos = static_cast<uint32_t>(rk);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = tid * E + e;
-    if (inK[e]) {
+    const int j = j0 + e;
+    if (inK(e)) {
       irow[kpos] = j;
       wrow[kpos] = 1.0f;
       ++kpos;
     }
-    if (a.m > 0 && inR[e] && !capped[e]) {
-      if (upos < delta) pi[e] += 1;
+    if (a.m > 0 && inR(e) && !capped(e)) {
+      if (upos < delta) pim1[e] += 1u;
       ++upos;
     }
   }
@@ -369,24 +441,25 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
     // ---- 3. systematic sample over the cumulative pi axis ----
     uint64_t psum = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) psum += pi[e];
+    for (int e = 0; e < E; ++e)
+      if (inR(e)) psum += static_cast<uint64_t>(pim1[e]) + 1u;
     uint64_t ptotal;
-    uint64_t c = block_exscan(psum, red64, ptotal);
+    uint64_t c = block_exscan(psum, red, par, ptotal);
     const uint64_t u = philox_word0(static_cast<uint32_t>(i), static_cast<uint32_t>(hd),
                                     static_cast<uint32_t>(b), 0u, a.seed_lo, a.seed_hi);
     auto below = [u](uint64_t x) -> uint64_t { return x > u ? ((x - u - 1) >> 32) + 1 : 0; };
-    // every key is in registers and the exscan's barriers have passed: the
+    // every key is in registers and the exscan's barrier has passed: the
     // staging array hands pi - 1 of each sampled slot (1 <= pi <= 2^32) to the
     // thread that writes its weight (k + m <= nV slots)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (!inR[e]) continue;
+      if (!inR(e)) continue;
       const uint64_t c0 = c;
-      c += pi[e];
+      c += static_cast<uint64_t>(pim1[e]) + 1u;
       const uint64_t n0 = below(c0), n1 = below(c);
       if (n1 > n0 && n0 < static_cast<uint64_t>(a.m)) {  // n0 < m always holds when sum pi = m 2^32
-        irow[a.k + static_cast<int>(n0)] = tid * E + e;
-        sbits[n0] = static_cast<uint32_t>(pi[e] - 1);
+        irow[a.k + static_cast<int>(n0)] = j0 + e;
+        sbits[n0] = pim1[e];
       }
     }
     __syncthreads();
@@ -437,56 +510,92 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  // Small per-unit state, as in select_kernel: validity from the unit index,
+  // bit masks for the exact set and the capped units, pi - 1 in 32 bits.
+  const int j0 = lane * E;
+  auto valid = [&](int e) { return j0 + e < a.nV; };
   uint32_t key[E];
-  bool valid[E], inK[E];
+  uint32_t fK = 0, fcap = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = lane * E + e;
-    const uint32_t raw = sb[j];  // inside the wave's slice; ignored past nV
-    valid[e] = j < a.nV;
-    key[e] = valid[e] ? sanitize(raw) : 0u;
-    inK[e] = false;
+    const uint32_t raw = sb[j0 + e];  // inside the wave's slice; ignored past nV
+    key[e] = valid(e) ? sanitize(raw) : 0u;
   }
 
-  // ---- 1. exact set ----
+  // ---- 1. exact set: the top bits over every key, the low bits over the
+  // keys in the threshold's bin (compacted into the wave's slice) ----
   if (a.k > 0) {
     uint32_t T = 0;
-    for (int bit = 30; bit >= 0; --bit) {
+    for (int bit = 30; bit >= SPLIT; --bit) {
       const uint32_t cand = T | (1u << bit);
       uint32_t c = 0;  // cand >= 1, and invalid units hold key 0
 #pragma unroll
       for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
       if (c >= static_cast<uint32_t>(a.k)) T = cand;
     }
+    {
+      const uint32_t hi = T + (1u << SPLIT);  // may be 2^31: no key reaches it
+      uint32_t above = 0, n_play = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        above += __popcll(__ballot(valid(e) && key[e] >= hi));
+        n_play += (valid(e) && key[e] >= T && key[e] < hi) ? 1u : 0u;
+      }
+      uint64_t play64;
+      uint32_t p = static_cast<uint32_t>(wave_exscan(n_play, play64));
+      const uint32_t play = static_cast<uint32_t>(play64);  // <= nV <= 64 E: fits the slice
+      // every key is in registers: the slice takes the in-play keys
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (valid(e) && key[e] >= T && key[e] < hi) sb[p++] = key[e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const uint32_t need = static_cast<uint32_t>(a.k) - above;  // >= 1
+      const int chunks = static_cast<int>((play + 63) / 64);   // uniform
+      uint32_t ck[E];
+#pragma unroll
+      for (int z = 0; z < E; ++z) {
+        const uint32_t x = static_cast<uint32_t>(lane + 64 * z);
+        ck[z] = (z < chunks && x < play) ? sb[x] : 0u;  // padding 0 never reaches cand >= 1
+      }
+      for (int bit = SPLIT - 1; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        uint32_t c = 0;
+#pragma unroll
+        for (int z = 0; z < E; ++z)
+          if (z < chunks) c += __popcll(__ballot(ck[z] >= cand));
+        if (c >= need) T = cand;
+      }
+    }
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      gt += __popcll(__ballot(valid[e] && key[e] > T));
-      eq += (valid[e] && key[e] == T) ? 1u : 0u;
+      gt += __popcll(__ballot(valid(e) && key[e] > T));
+      eq += (valid(e) && key[e] == T) ? 1u : 0u;
     }
     const uint32_t need = static_cast<uint32_t>(a.k) - gt;
     uint64_t eq_total;
     uint32_t r = static_cast<uint32_t>(wave_exscan(eq, eq_total));
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (!valid[e]) continue;
+      if (!valid(e)) continue;
       if (key[e] > T) {
-        inK[e] = true;
+        fK |= 1u << e;
       } else if (key[e] == T) {
-        inK[e] = r < need;
+        if (r < need) fK |= 1u << e;
         ++r;
       }
     }
   }
+  auto inK = [&](int e) { return ((fK >> e) & 1u) != 0u; };
+  auto inR = [&](int e) { return valid(e) && !inK(e); };
+  auto capped = [&](int e) { return ((fcap >> e) & 1u) != 0u; };
 
-  bool inR[E], capped[E];
-  uint64_t pi[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    inR[e] = valid[e] && !inK[e];
-    capped[e] = false;
-    pi[e] = 0;
-  }
+  uint32_t pim1[E];  // pi - 1 on R (pi in [1, 2^32])
 
   uint64_t delta = 0;
   if (a.m > 0) {
@@ -494,14 +603,14 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
     uint32_t mx = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (inR[e]) mx = max(mx, key[e]);
+      if (inR(e)) mx = max(mx, key[e]);
     mx = wave_max_u32(mx);
     uint32_t q[E];
     const int ex = mx ? frexp_exp(mx) : 0;
     uint64_t qsum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      q[e] = inR[e] ? (mx ? quantise(key[e], ex) : 1u) : 0u;
+      q[e] = inR(e) ? (mx ? quantise(key[e], ex) : 1u) : 0u;
       qsum += q[e];
     }
     uint64_t QU = wave_sum(qsum);
@@ -514,10 +623,10 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
       uint32_t cnt = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool cap = inR[e] && !capped[e] && mt * q[e] >= QU;
+        const bool cap = inR(e) && !capped(e) && mt * q[e] >= QU;
         cnt += __popcll(__ballot(cap));
         if (cap) {
-          capped[e] = true;
+          fcap |= 1u << e;
           qcap += q[e];
         }
       }
@@ -536,13 +645,12 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
     uint64_t usum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (!inR[e]) continue;
-      if (capped[e]) {
-        pi[e] = 1ull << 32;
-      } else {
+      pim1[e] = 0xFFFFFFFFu;  // capped: pi = 2^32
+      if (inR(e) && !capped(e)) {
         const double ratio = (mt_d * static_cast<double>(q[e])) / qu_d;
-        pi[e] = static_cast<uint32_t>(ratio * 4294967296.0);
-        usum += pi[e];
+        const uint32_t pv = static_cast<uint32_t>(ratio * 4294967296.0);
+        pim1[e] = pv - 1u;
+        usum += pv;
       }
     }
     delta = (mt << 32) - wave_sum(usum);
@@ -552,8 +660,8 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
   uint32_t nk = 0, nu = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    nk += inK[e] ? 1u : 0u;
-    nu += (inR[e] && !capped[e]) ? 1u : 0u;
+    nk += inK(e) ? 1u : 0u;
+    nu += (inR(e) && !capped(e)) ? 1u : 0u;
   }
   uint64_t rk_total;
   const uint64_t rk = wave_exscan((static_cast<uint64_t>(nk) << 32) | nu, rk_total);
@@ -561,14 +669,14 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
   uint32_t upos = static_cast<uint32_t>(rk);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = lane * E + e;
-    if (inK[e]) {
+    const int j = j0 + e;
+    if (inK(e)) {
       irow[kpos] = j;
       wrow[kpos] = 1.0f;
       ++kpos;
     }
-    if (a.m > 0 && inR[e] && !capped[e]) {
-      if (upos < delta) pi[e] += 1;
+    if (a.m > 0 && inR(e) && !capped(e)) {
+      if (upos < delta) pim1[e] += 1u;
       ++upos;
     }
   }
@@ -577,7 +685,8 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
     // ---- 3. systematic sample over the cumulative pi axis ----
     uint64_t psum = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) psum += pi[e];
+    for (int e = 0; e < E; ++e)
+      if (inR(e)) psum += static_cast<uint64_t>(pim1[e]) + 1u;
     uint64_t ptotal;
     uint64_t c = wave_exscan(psum, ptotal);
     const uint64_t u = philox_word0(static_cast<uint32_t>(i), static_cast<uint32_t>(hd),
@@ -590,13 +699,13 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (!inR[e]) continue;
+      if (!inR(e)) continue;
       const uint64_t c0 = c;
-      c += pi[e];
+      c += static_cast<uint64_t>(pim1[e]) + 1u;
       const uint64_t n0 = below(c0), n1 = below(c);
       if (n1 > n0 && n0 < static_cast<uint64_t>(a.m)) {  // k + m <= nV <= 64 E slots
-        irow[a.k + static_cast<int>(n0)] = lane * E + e;
-        sb[n0] = static_cast<uint32_t>(pi[e] - 1);
+        irow[a.k + static_cast<int>(n0)] = j0 + e;
+        sb[n0] = pim1[e];
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
