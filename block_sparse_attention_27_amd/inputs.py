@@ -22,6 +22,11 @@ the layer shapes those models use:
   V = nu_c + e_v with a per-cluster value nu_c ~ N(0, I_d) and
   e_v ~ N(0, 0.5^2 I_d) (value_mode "clustered": values that follow the
   clusters, so that dense attention outputs are far from zero);
+* key_spread "uniform" (every preset) gives every key the noise std above;
+  key_spread "clustered" gives the keys of cluster c their own noise std
+  noise_std * 2^u_c with u_c ~ U(0, 3) (0.5 to 4 at the default), so key
+  units differ in their within-unit spread and not only in their means (Q, V
+  and the centroids are the same draws as with "uniform");
 * the logit scale is sm_scale = 1/temperature;
 * bf16 workloads are drawn in fp32 and rounded to nearest-even bf16;
 * the HunyuanVideo-shaped workload also carries a gather index that groups
@@ -31,7 +36,8 @@ the layer shapes those models use:
 Random streams: one numpy PCG64 stream seeded with ``[seed]`` draws the
 cluster seed points and the cluster relabelling; each (b, h) draws its
 centroids and noise from its own stream seeded with ``[seed, 1, b, h]``, so any
-head can be made alone; clustered values draw nu_c from ``[seed, 2, b, h]``.
+head can be made alone; clustered values draw nu_c from ``[seed, 2, b, h]``,
+clustered key spreads draw u_c from ``[seed, 3, b, h]``.
 """
 
 from __future__ import annotations
@@ -77,6 +83,7 @@ class Workload:
     seed: int = 0
     select_seed: int = 0
     value_mode: str = "noise"  # "noise" or "clustered"
+    key_spread: str = "uniform"  # "uniform" or "clustered"
 
     @property
     def N(self) -> int:
@@ -218,11 +225,18 @@ def generate(w: Workload, heads: Optional[Iterable[int]] = None) -> dict:
         rng = np.random.default_rng([w.seed, 1, b, h])
         mu = rng.standard_normal((w.clusters, d), dtype=np.float32) * np.float32(w.centroid_std)
         base = mu[cid]
+        if w.key_spread == "clustered":
+            u = np.random.default_rng([w.seed, 3, b, h]).uniform(0.0, 3.0, w.clusters)
+            k_std = (np.float32(w.noise_std) * np.exp2(u).astype(np.float32))[cid][:, None]
+        elif w.key_spread == "uniform":
+            k_std = np.float32(w.noise_std)
+        else:
+            raise ValueError(f"unknown key_spread {w.key_spread!r}")
         out = []
-        for noisy in (True, True, False):  # Q, K share the centroid; V is pure noise
+        for which in ("q", "k", "v"):  # Q, K share the centroid; V is pure noise
             x = rng.standard_normal((N, d), dtype=np.float32)
-            if noisy:
-                x *= np.float32(w.noise_std)
+            if which != "v":
+                x *= k_std if which == "k" else np.float32(w.noise_std)
                 x += base
                 x *= inv_sqrt_d
             out.append(x)

@@ -26,6 +26,17 @@ through ``bsa_attend`` (fp32 output) and reports, against
                   seeds tends to 1), truncation and the unweighted sample
                   are biased low
 
+For each scorer (plain, ibcs, stats) the study also reports how well its
+ranking finds the heavy units: ``mass_<scorer>`` is the mean share of a query
+block's true attention (dense softmax over the valid keys, summed per key unit,
+averaged over the block's rows) held by the scorer's top-(k+m) units, next to
+``mass_best``, the share the true top-(k+m) units hold; ``exact_diff_stats``
+is the fraction of query blocks whose top-k set under the statistics-aware
+scorer differs from the plain scorer's. The true masses come from fp32
+softmax(Q K^T) in PyTorch, a reporting aid outside the library's path.
+``--key-spread clustered`` gives key units unequal within-unit spread, the
+case the statistics-aware scorer is built for.
+
 The sampled estimators are averaged over several selection seeds (``_std`` is
 the standard deviation of the error over seeds). ``top_mass`` is the mean
 share of a query block's estimated attention mass (its score row) held by its
@@ -79,6 +90,36 @@ def _rel_err_per_head(o, ref, n_valid):
     return (num / den).flatten().tolist()
 
 
+def unit_mass(w, q, k, perm, rows_per_chunk=2048):
+    """True attention mass per (b, h, query block, key unit): the dense softmax of
+    sm_scale <q, k> over the valid keys, summed over each unit's keys and averaged
+    over the block's valid rows (fp32, in chunks of query rows)."""
+    import torch
+
+    B, H, Np, d = q.shape
+    if perm is not None:
+        q = q.index_select(2, perm.long())
+        k = k.index_select(2, perm.long())
+    nqb, nku = Np // w.block_q, Np // w.block_k
+    M = torch.zeros((B, H, nqb, nku), dtype=torch.float32, device=q.device)
+    key_ok = torch.arange(Np, device=q.device) < w.N
+    for b in range(B):
+        for h in range(H):
+            kt = k[b, h].float().t().contiguous()  # [d, Np], contiguous right operand
+            for r0 in range(0, Np, rows_per_chunk):
+                r1 = min(Np, r0 + rows_per_chunk)
+                logits = torch.matmul(q[b, h, r0:r1].float(), kt) * w.sm_scale
+                logits.masked_fill_(~key_ok, float("-inf"))
+                p = torch.softmax(logits, dim=-1)
+                pu = p.view(r1 - r0, nku, w.block_k).sum(-1)  # [rows, units]
+                rows = torch.arange(r0, r1, device=q.device)
+                pu = pu * (rows < w.N).float()[:, None]
+                blk = pu.view(-1, w.block_q, nku).sum(1)
+                cnt = (rows < w.N).float().view(-1, w.block_q).sum(1).clamp(min=1)
+                M[b, h, r0 // w.block_q: r1 // w.block_q] = blk / cnt[:, None]
+    return M
+
+
 def run_temperature(w, seeds, log=print, keep_lists=False):
     """All estimators for one workload (one temperature). Returns a result dict.
 
@@ -111,12 +152,24 @@ def run_temperature(w, seeds, log=print, keep_lists=False):
             kept.append((name, seed, bsa.Problem.from_buffer_copy(p), idx.cpu().numpy(), wt.cpu().numpy()))
         return statistics.mean(_rel_err_per_head(o, dense, w.N)), _d_ratio(lse, lse_d, w.N)
 
-    res = {"workload": w.name, "values": w.value_mode, "temperature": w.temperature, "k_exact": w.k_exact,
-           "m_sample": w.m_sample, "density": round(w.density, 4), "top_mass": round(top_mass, 4),
-           "seeds": len(seeds)}
+    res = {"workload": w.name, "values": w.value_mode, "key_spread": w.key_spread, "temperature": w.temperature,
+           "k_exact": w.k_exact, "m_sample": w.m_sample, "density": round(w.density, 4),
+           "top_mass": round(top_mass, 4), "seeds": len(seeds)}
 
     S_ib = bsa.score_ibcs(base, q, k, perm, groups=4, iters=3)[0]
     S_st = bsa.score_stats(base, q, k, perm)[0]
+
+    M = unit_mass(w, q, k, perm)
+    n_l = min(L, S.shape[-1])
+    res["mass_best"] = float(torch.topk(M, n_l, dim=-1).values.sum(-1).mean())
+    for name, Sx in (("plain", S), ("ibcs", S_ib), ("stats", S_st)):
+        top = torch.topk(Sx, n_l, dim=-1).indices
+        res["mass_" + name] = float(M.gather(-1, top).sum(-1).mean())
+    if w.k_exact > 0:
+        ex_p = torch.topk(S, w.k_exact, dim=-1).indices.sort(-1).values
+        ex_s = torch.topk(S_st, w.k_exact, dim=-1).indices.sort(-1).values
+        res["exact_diff_stats"] = float((ex_p != ex_s).any(-1).float().mean())
+    del M
 
     p_tr = bsa.problem_for(w, out_fp32=1, k_exact=L, m_sample=0)
     idx, wt = bsa.select(p_tr, S)
@@ -159,6 +212,7 @@ def main(argv=None):
     ap.add_argument("--temps", type=float, nargs="+", default=[0.5, 1.0, 2.0])
     ap.add_argument("--seeds", type=int, default=8, help="selection seeds per sampled estimator")
     ap.add_argument("--values", nargs="+", default=["noise", "clustered"], choices=["noise", "clustered"])
+    ap.add_argument("--key-spread", default="uniform", choices=["uniform", "clustered"])
     args = ap.parse_args(argv)
 
     import torch
@@ -168,7 +222,7 @@ def main(argv=None):
     base = WORKLOADS[args.workload]
     for vm in args.values:
         for tau in args.temps:
-            w = base.replace(temperature=tau, value_mode=vm)
+            w = base.replace(temperature=tau, value_mode=vm, key_spread=args.key_spread)
             print(f"[study] {w.name} values={vm} tau={tau}", file=sys.stderr, flush=True)
             res = run_temperature(w, list(range(args.seeds)),
                                   log=lambda m: print(m, file=sys.stderr, flush=True))

@@ -77,3 +77,19 @@ def test_study_numbers_against_the_oracle(values):
     # the pages' claims in this regime: the weighted estimators keep the denominator (D_hat / D near 1)
     # while truncation and the unweighted sample lose part of it
     assert per["truncation"][0][1] < 1.0 and np.mean([d for _, d in per["unweighted"]]) < 1.0
+
+
+def test_statistics_aware_scorer_reranks_units_with_unequal_spread():
+    # Veda, Abstract (statistics-aware tile scoring): with key units of unequal within-unit spread the
+    # second-moment term changes which units are exact far more often than with a uniform spread; the
+    # true (dense) attention mass its picks hold is reported, not asserted: at these spreads it moves by
+    # about 1e-4 either way
+    from block_sparse_attention_27_amd.inputs import WORKLOADS
+    print_case("statistics-aware vs plain scorer, uniform and clustered key spread")
+    base = WORKLOADS["wan14b_480p"].replace(H=4, temperature=0.5, value_mode="clustered")
+    r_u = run_temperature(base, [0], log=lambda m: None)
+    r_c = run_temperature(base.replace(key_spread="clustered"), [0], log=lambda m: None)
+    print_case(f"  exact sets differ: uniform {r_u['exact_diff_stats']:.4f}, clustered {r_c['exact_diff_stats']:.4f}; "
+               f"true mass plain/stats {r_c['mass_plain']:.5f}/{r_c['mass_stats']:.5f}")
+    assert r_c["exact_diff_stats"] > 2 * r_u["exact_diff_stats"] and r_c["exact_diff_stats"] > 0.05
+    assert r_c["mass_plain"] <= r_c["mass_best"] + 1e-6 and r_c["mass_stats"] <= r_c["mass_best"] + 1e-6

@@ -63,3 +63,26 @@ def test_clustered_values_follow_clusters_and_leave_q_k_alone():
     assert 0.35 < within < 0.65
     with pytest.raises(ValueError):
         generate(w.replace(value_mode="other"))
+
+
+def test_clustered_key_spread_changes_only_the_key_noise():
+    w = WORKLOADS["tiny"].replace(grid=(2, 8, 8), clusters=4)
+    a, b = generate(w), generate(w.replace(key_spread="clustered"))
+    assert np.array_equal(a["q"], b["q"]) and np.array_equal(a["v"], b["v"])
+    assert np.array_equal(b["k"], generate(w.replace(key_spread="clustered"))["k"])
+    cid = cluster_ids(w)
+    ka, kb = (as_float32(x["k"])[0, 0, : w.N].astype(np.float64) * np.sqrt(w.d) for x in (a, b))
+    # the same centroids and the same unit normals: the deviations differ by one factor per cluster
+    stds = []
+    for c in np.unique(cid):
+        rows = cid == c
+        if rows.sum() < 8:
+            continue
+        dev_a = ka[rows] - ka[rows].mean(axis=0)
+        dev_b = kb[rows] - kb[rows].mean(axis=0)
+        ratio = np.linalg.norm(dev_b) / np.linalg.norm(dev_a)
+        assert 0.9 < ratio < 8.5, ratio  # 2^u with u in [0, 3], up to the rounding of the noise draw
+        stds.append(ratio)
+    assert max(stds) / min(stds) > 1.5  # the spreads really differ between clusters
+    with pytest.raises(ValueError):
+        generate(w.replace(key_spread="other"))
