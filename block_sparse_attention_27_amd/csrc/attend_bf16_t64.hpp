@@ -453,6 +453,43 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
     orow = gather_row<PERM>(a, qrow, ok);
     inv = lsum > 0.f ? 1.f / lsum : 0.f;
   }
+  if constexpr (OUT32) {
+    // fp32 rows go out whole: each wave stages its 32 rows (row-major, 16-byte
+    // chunk c of row n at chunk c ^ (n mod CPR), conflict-free both ways) in its
+    // own tile slot, then every store instruction writes 64 / CPR complete rows.
+    constexpr int CPR = D / 4;  // 16-byte chunks per fp32 row
+    __syncthreads();            // every wave is done with the tile slots
+    char* stage = wave == 0 ? k_lds0 : wave == 1 ? k_lds1 : wave == 2 ? v_lds0 : v_lds1;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = (32 * dt + 8 * g + 4 * h) / 4;
+        float4 x = make_float4(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv, o[dt][4 * g + 2] * inv,
+                               o[dt][4 * g + 3] * inv);
+        *reinterpret_cast<float4*>(stage + n * (4 * D) + 16 * (c ^ (n % CPR))) = x;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int RPS = 64 / CPR;  // rows per store instruction
+#pragma unroll
+    for (int z = 0; z < 32 / RPS; ++z) {
+      const int rr = z * RPS + lane / CPR, c = lane % CPR;
+      const int grow = qi * 128 + 32 * wave + rr;  // this lane's query row
+      bool rok = true;
+      int orow_r = grow;
+      if (grow < a.N) orow_r = gather_row<PERM>(a, grow, rok);
+      const float4 x = *reinterpret_cast<const float4*>(stage + rr * (4 * D) + 16 * (c ^ (rr % CPR)));
+      if (rok) *reinterpret_cast<float4*>(static_cast<float*>(a.out) + bh_off + static_cast<size_t>(orow_r) * D + 4 * c) = x;
+    }
+    if (a.lse != nullptr && h == 0 && ok) {
+      a.lse[static_cast<size_t>(bh) * a.N_pad + orow] =
+          (qrow < a.N && lsum > 0.f) ? (m_ref + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f : -INFINITY;
+    }
+    return;
+  }
   if (ok) {  // rows >= N (inv = 0) are written as zeros
     const size_t obase = bh_off + static_cast<size_t>(orow) * D;
 #pragma unroll
