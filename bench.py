@@ -1,7 +1,8 @@
 """Benchmark: one weighted block-sparse attention layer per step on one MI355X.
 
-A step is the whole sparse pass -- bsa_score, bsa_select, bsa_attend -- over a
-synthetic clustered-token layer shaped like Wan2.1-T2V-14B at 720p (B=1, H=40,
+A step is the whole sparse pass -- bsa_score, bsa_select, bsa_attend, preceded
+on a permuted sequence by bsa_permute_rows of K and V -- over a synthetic
+clustered-token layer shaped like Wan2.1-T2V-14B at 720p (B=1, H=40,
 N=75,600 -> 75,648, d=128, bf16, 128-token blocks, 20 exact + 40 sampled key
 blocks per query block, ~10% density). Inputs are resident in HBM before the
 timed region. The dense flash-attention kernel of the same library is timed
@@ -156,14 +157,30 @@ def main(argv=None):
     wt = torch.empty((w.B, w.H, w.n_qblocks, w.list_len), dtype=torch.float32, device="cuda")
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    # A permuted sequence: K and V are put into the permuted order once per
+    # pass (bsa_permute_rows) and the steps run with kv_permuted = 1, so the
+    # attention pass reads every key unit as contiguous rows; Q is gathered and
+    # out scattered inside the kernels.
+    if perm is not None:
+        kk, vv = torch.empty_like(k), torch.empty_like(v)
+        pp, pp16 = bsa.with_kv_permuted(p), bsa.with_kv_permuted(p16)
+    else:
+        kk, vv, pp, pp16 = k, v, p, p16
+
+    def permute():
+        if perm is not None:
+            bsa.bsa_permute_rows(p, k, perm, kk)
+            bsa.bsa_permute_rows(p, v, perm, vv)
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        bsa.bsa_score(p, q, k, perm, S, qm, km)
+        permute()
+        if ev: ev[4].record(stream)
+        bsa.bsa_score(pp, q, kk, perm, S, qm, km)
         if ev: ev[1].record(stream)
-        bsa.bsa_select(p, S, idx, wt)
+        bsa.bsa_select(pp, S, idx, wt)
         if ev: ev[2].record(stream)
-        bsa.bsa_attend(p, q, k, v, perm, idx, wt, out, None)
+        bsa.bsa_attend(pp, q, kk, vv, perm, idx, wt, out, None)
         if ev: ev[3].record(stream)
 
     _log(f"warmup {args.warmup}")
@@ -172,14 +189,15 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     _log(f"timing {args.steps} steps")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
         step(e)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    t_score = statistics.mean(e[0].elapsed_time(e[1]) for e in evs)
+    t_permute = statistics.mean(e[0].elapsed_time(e[4]) for e in evs)
+    t_score = statistics.mean(e[4].elapsed_time(e[1]) for e in evs)
     t_select = statistics.mean(e[1].elapsed_time(e[2]) for e in evs)
     t_attend = statistics.mean(e[2].elapsed_time(e[3]) for e in evs)
     t_pass = statistics.mean(e[0].elapsed_time(e[3]) for e in evs)
@@ -188,10 +206,11 @@ def main(argv=None):
     # Infinity Cache; each call is timed on its own
     n_cold = max(3, min(args.steps, 5))
     flush = torch.empty(1 << 27, dtype=torch.float32, device="cuda")
-    cold = {"score": [], "select": [], "attend": []}
-    calls = (("score", lambda: bsa.bsa_score(p, q, k, perm, S, qm, km)),
-             ("select", lambda: bsa.bsa_select(p, S, idx, wt)),
-             ("attend", lambda: bsa.bsa_attend(p, q, k, v, perm, idx, wt, out, None)))
+    cold = {"permute": [], "score": [], "select": [], "attend": []}
+    calls = (("permute", permute),
+             ("score", lambda: bsa.bsa_score(pp, q, kk, perm, S, qm, km)),
+             ("select", lambda: bsa.bsa_select(pp, S, idx, wt)),
+             ("attend", lambda: bsa.bsa_attend(pp, q, kk, vv, perm, idx, wt, out, None)))
     for _ in range(n_cold):
         for name, call in calls:
             flush.fill_(1.0)
@@ -205,13 +224,17 @@ def main(argv=None):
     del flush
 
     # sampling-plan reuse: one score + select, then r attend calls with that plan
+    # (each on its own step's K and V, so a permuted sequence permutes them each time)
     reuse_r = 4
     re = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     re[0].record(stream)
-    bsa.bsa_score(p, q, k, perm, S, qm, km)
-    bsa.bsa_select(p, S, idx, wt)
-    for _ in range(reuse_r):
-        bsa.bsa_attend(p, q, k, v, perm, idx, wt, out, None)
+    permute()
+    bsa.bsa_score(pp, q, kk, perm, S, qm, km)
+    bsa.bsa_select(pp, S, idx, wt)
+    for i in range(reuse_r):
+        if i:
+            permute()
+        bsa.bsa_attend(pp, q, kk, vv, perm, idx, wt, out, None)
     re[1].record(stream)
     torch.cuda.synchronize()
     t_reuse = re[0].elapsed_time(re[1]) / reuse_r
@@ -221,11 +244,11 @@ def main(argv=None):
     qc = torch.empty((w.B, w.H, w.n_qblocks, ib_g, w.d), dtype=torch.float32, device="cuda")
     qs = torch.empty((w.B, w.H, w.n_qblocks, ib_g), dtype=torch.int32, device="cuda")
     for _ in range(2):
-        bsa.bsa_score_ibcs(p, ib_g, ib_t, q, k, perm, S, qc, qs, km)
+        bsa.bsa_score_ibcs(pp, ib_g, ib_t, q, kk, perm, S, qc, qs, km)
     ie = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
     for e in ie:
         e[0].record(stream)
-        bsa.bsa_score_ibcs(p, ib_g, ib_t, q, k, perm, S, qc, qs, km)
+        bsa.bsa_score_ibcs(pp, ib_g, ib_t, q, kk, perm, S, qc, qs, km)
         e[1].record(stream)
     torch.cuda.synchronize()
     t_ibcs = statistics.mean(e[0].elapsed_time(e[1]) for e in ie)
@@ -234,11 +257,11 @@ def main(argv=None):
     # statistics-aware scorer (key-unit variances) in place of bsa_score
     kv = torch.empty_like(km)
     for _ in range(2):
-        bsa.bsa_score_stats(p, q, k, perm, S, qm, km, kv)
+        bsa.bsa_score_stats(pp, q, kk, perm, S, qm, km, kv)
     se = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
     for e in se:
         e[0].record(stream)
-        bsa.bsa_score_stats(p, q, k, perm, S, qm, km, kv)
+        bsa.bsa_score_stats(pp, q, kk, perm, S, qm, km, kv)
         e[1].record(stream)
     torch.cuda.synchronize()
     t_stats = statistics.mean(e[0].elapsed_time(e[1]) for e in se)
@@ -249,11 +272,23 @@ def main(argv=None):
     be = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
     for e in be:
         e[0].record(stream)
-        bsa.bsa_attend(p16, q, k, v, perm, idx, wt, out16, None)
+        bsa.bsa_attend(pp16, q, kk, vv, perm, idx, wt, out16, None)
         e[1].record(stream)
     torch.cuda.synchronize()
     t_attend16 = statistics.mean(e[0].elapsed_time(e[1]) for e in be)
     del out16
+
+    # the same lists with K and V gathered inside the attention pass (kv_permuted = 0)
+    t_attend_gather = None
+    if perm is not None:
+        ge = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(max(3, min(args.steps, 10)))]
+        bsa.bsa_attend(p, q, k, v, perm, idx, wt, out, None)
+        for e in ge:
+            e[0].record(stream)
+            bsa.bsa_attend(p, q, k, v, perm, idx, wt, out, None)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        t_attend_gather = statistics.mean(e[0].elapsed_time(e[1]) for e in ge)
 
     t_dense = None
     if not args.no_dense:
@@ -308,13 +343,16 @@ def main(argv=None):
                    "block_q": w.block_q, "block_k": w.block_k, "k_exact": w.k_exact,
                    "m_sample": w.m_sample, "density": round(w.density, 4), "temperature": w.temperature,
                    "permuted": w.permute, "parallelism": "single GPU"},
+        "t_permute_ms": round(t_permute, 4) if perm is not None else None,
         "t_score_ms": round(t_score, 4),
         "t_select_ms": round(t_select, 4),
         "t_attend_ms": round(t_attend, 4),
         "t_attend_bf16_out_ms": round(t_attend16, 4),
+        "t_attend_gather_inside_ms": None if t_attend_gather is None else round(t_attend_gather, 4),
         "t_dense_ms": None if t_dense is None else round(t_dense, 4),
         "score_select_share": round((t_score + t_select) / t_pass, 4),
-        "cold": {"t_score_ms": round(t_cold["score"], 4), "t_select_ms": round(t_cold["select"], 4),
+        "cold": {"t_permute_ms": round(t_cold["permute"], 4) if perm is not None else None,
+                 "t_score_ms": round(t_cold["score"], 4), "t_select_ms": round(t_cold["select"], 4),
                  "t_attend_ms": round(t_cold["attend"], 4),
                  "t_pass_ms": round(sum(t_cold.values()), 4), "calls": n_cold,
                  "flush": "512 MB written before every call"},

@@ -11,11 +11,14 @@ in by the caller):
     bsa_score_ibcs(problem, groups, iters, q, k, perm, S, q_cent, q_size, k_mean)
     bsa_score_stats(problem, q, k, perm, S, q_mean, k_mean, k_var)
     bsa_select(problem, S, idx, w)
+    bsa_permute_rows(problem, x, perm, x_perm)
     bsa_attend(problem, q, k, v, perm, idx, w, out, lse)
     bsa_attend_dense(problem, q, k, v, perm, out, lse)
-Convenience wrappers that allocate their outputs: score, score_ibcs, score_stats, select, attend,
-attend_dense, sparse_attention (the three steps in order), and SamplingPlan,
-which keeps one score + select result for reuse by later attend calls.
+Convenience wrappers that allocate their outputs: score, score_ibcs, score_stats, select,
+permute_rows, attend, attend_dense, sparse_attention (the three steps in order; with a
+permutation it first puts K and V into the permuted order and runs the steps with
+kv_permuted = 1), and SamplingPlan, which keeps one score + select result for reuse by
+later attend calls.
 """
 
 from __future__ import annotations
@@ -28,8 +31,9 @@ from .inputs import Workload
 
 __all__ = [
     "Problem", "BsaError", "load_library", "library_path", "problem_for", "out_dtype",
-    "bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_attend", "bsa_attend_dense",
-    "score", "score_ibcs", "score_stats", "select", "attend", "attend_dense", "sparse_attention", "SamplingPlan",
+    "bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_permute_rows", "bsa_attend",
+    "bsa_attend_dense", "score", "score_ibcs", "score_stats", "select", "permute_rows", "with_kv_permuted",
+    "attend", "attend_dense", "sparse_attention", "SamplingPlan",
     "BSA_OK", "BSA_ERR_INVALID_ARG", "BSA_ERR_UNSUPPORTED", "BSA_ERR_HIP", "BSA_BF16", "BSA_FP32",
 ]
 
@@ -50,7 +54,7 @@ class Problem(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
         ("N_pad", ctypes.c_int32), ("d", ctypes.c_int32), ("block_q", ctypes.c_int32),
         ("block_k", ctypes.c_int32), ("k_exact", ctypes.c_int32), ("m_sample", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("out_fp32", ctypes.c_int32), ("kv_permuted", ctypes.c_int32),
         ("seed", ctypes.c_uint64), ("sm_scale", ctypes.c_float),
     ]
 
@@ -99,6 +103,8 @@ def load_library():
     lib.bsa_score_stats.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_select.restype = ctypes.c_int
     lib.bsa_select.argtypes = [P, vp, vp, vp, vp]
+    lib.bsa_permute_rows.restype = ctypes.c_int
+    lib.bsa_permute_rows.argtypes = [P, vp, vp, vp, vp]
     lib.bsa_attend.restype = ctypes.c_int
     lib.bsa_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_attend_dense.restype = ctypes.c_int
@@ -119,7 +125,7 @@ def problem_for(w: Workload, seed: Optional[int] = None, **overrides) -> Problem
     f = dict(B=w.B, H=w.H, N=w.N, N_pad=w.N_pad, d=w.d, block_q=w.block_q, block_k=w.block_k,
              k_exact=w.k_exact, m_sample=w.m_sample,
              dtype=BSA_BF16 if w.dtype == "bf16" else BSA_FP32,
-             out_fp32=0, seed=w.select_seed if seed is None else seed, sm_scale=w.sm_scale, reserved=0)
+             out_fp32=0, seed=w.select_seed if seed is None else seed, sm_scale=w.sm_scale, kv_permuted=0)
     f.update(overrides)
     return Problem(**f)
 
@@ -217,6 +223,16 @@ def bsa_select(p: Problem, S, idx, w, stream=None):
                                                    _stream(stream)))
 
 
+def bsa_permute_rows(p: Problem, x, perm, x_perm, stream=None):
+    import torch
+    et = _elem_dtype(p)
+    _expect("x", x, (p.B, p.H, p.N_pad, p.d), et)
+    _expect("perm", perm, (p.N_pad,), torch.int32)
+    _expect("x_perm", x_perm, (p.B, p.H, p.N_pad, p.d), et)
+    _check("bsa_permute_rows", load_library().bsa_permute_rows(ctypes.byref(p), _ptr(x), _ptr(perm), _ptr(x_perm),
+                                                               _stream(stream)))
+
+
 def bsa_attend(p: Problem, q, k, v, perm, idx, w, out, lse=None, stream=None):
     import torch
     et = _elem_dtype(p)
@@ -293,6 +309,21 @@ def select(p: Problem, S, stream=None):
     return idx, w
 
 
+def permute_rows(p: Problem, x, perm, stream=None):
+    """x_perm with x_perm[b, h, r] = x[b, h, perm[r]] for r < N (zero rows past N)."""
+    import torch
+    x_perm = torch.empty_like(x)
+    bsa_permute_rows(p, x, perm, x_perm, stream)
+    return x_perm
+
+
+def with_kv_permuted(p: Problem, flag: int = 1) -> Problem:
+    """A copy of ``p`` with kv_permuted set (K and V passed as K[perm], V[perm])."""
+    q = Problem.from_buffer_copy(p)
+    q.kv_permuted = flag
+    return q
+
+
 def attend(p: Problem, q, k, v, idx, w, perm=None, with_lse=False, stream=None):
     """Returns out (and lse when ``with_lse``)."""
     import torch
@@ -311,7 +342,16 @@ def attend_dense(p: Problem, q, k, v, perm=None, with_lse=False, stream=None):
 
 
 def sparse_attention(p: Problem, q, k, v, perm=None, with_lse=False, stream=None):
-    """score -> select -> attend on one stream; returns (out[, lse], idx, w)."""
+    """score -> select -> attend on one stream; returns (out[, lse], idx, w).
+
+    With a permutation (and K, V in token order, p.kv_permuted == 0) K and V are
+    first gathered into the permuted order, so that the attention pass reads
+    every key unit as contiguous rows; the results are those of the
+    permutation applied inside each call.
+    """
+    if perm is not None and not p.kv_permuted:
+        k, v = permute_rows(p, k, perm, stream), permute_rows(p, v, perm, stream)
+        p = with_kv_permuted(p)
     S, _, _ = score(p, q, k, perm, stream)
     idx, w = select(p, S, stream)
     res = attend(p, q, k, v, idx, w, perm, with_lse, stream)

@@ -13,33 +13,42 @@
 namespace bsa {
 namespace attend_bf16_impl {
 
-template <int D, int BQ, int BK, bool DENSE, bool PERM, bool OUT32>
+template <int D, int BQ, int BK, bool DENSE, int PM, bool OUT32>
 hipError_t launch_one(const AttendArgs& a, hipStream_t s) {
   if constexpr (BQ == 128) {
-    hipLaunchKernelGGL((attend_t64_kernel<D, BK, DENSE, PERM, OUT32>), dim3(a.n_wg), dim3(64 * NW64), 0, s, a);
+    hipLaunchKernelGGL((attend_t64_kernel<D, BK, DENSE, PM, OUT32>), dim3(a.n_wg), dim3(64 * NW64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((attend_w32_kernel<D, BQ, BK, DENSE, PERM, OUT32>), dim3(a.n_wg), dim3(BQ * 4), 0, s, a);
+    hipLaunchKernelGGL((attend_w32_kernel<D, BQ, BK, DENSE, PM, OUT32>), dim3(a.n_wg), dim3(BQ * 4), 0, s, a);
   }
   return hipGetLastError();
 }
 
-template <int D, int BQ, bool DENSE, bool PERM, bool OUT32>
+template <int D, int BQ, bool DENSE, int PM, bool OUT32>
 hipError_t dispatch_bk(const AttendArgs& a, int bk, hipStream_t s) {
   if constexpr (DENSE) {
-    return launch_one<D, BQ, 128, true, PERM, OUT32>(a, s);
+    return launch_one<D, BQ, 128, true, PM, OUT32>(a, s);
   } else {
     switch (bk) {
-      case 32: return launch_one<D, BQ, 32, false, PERM, OUT32>(a, s);
-      case 64: return launch_one<D, BQ, 64, false, PERM, OUT32>(a, s);
-      default: return launch_one<D, BQ, 128, false, PERM, OUT32>(a, s);
+      case 32: return launch_one<D, BQ, 32, false, PM, OUT32>(a, s);
+      case 64: return launch_one<D, BQ, 64, false, PM, OUT32>(a, s);
+      default: return launch_one<D, BQ, 128, false, PM, OUT32>(a, s);
     }
   }
 }
 
+// Permutation modes. Dense attention never gathers K and V: a softmax over
+// every valid key does not depend on the order of the keys, so with a
+// permutation only the query rows are gathered and the output rows scattered.
+// The sparse pass gathers K and V through perm unless they arrive permuted.
 template <int D, int BQ, bool OUT32>
-hipError_t dispatch_mode(const AttendArgs& a, int bk, bool dense, bool perm, hipStream_t s) {
-  if (dense) return perm ? dispatch_bk<D, BQ, true, true, OUT32>(a, bk, s) : dispatch_bk<D, BQ, true, false, OUT32>(a, bk, s);
-  return perm ? dispatch_bk<D, BQ, false, true, OUT32>(a, bk, s) : dispatch_bk<D, BQ, false, false, OUT32>(a, bk, s);
+hipError_t dispatch_mode(const AttendArgs& a, int bk, bool dense, bool perm, bool kv_permuted, hipStream_t s) {
+  if (dense) {
+    return perm ? dispatch_bk<D, BQ, true, PERM_QO, OUT32>(a, bk, s)
+                : dispatch_bk<D, BQ, true, PERM_NONE, OUT32>(a, bk, s);
+  }
+  if (!perm) return dispatch_bk<D, BQ, false, PERM_NONE, OUT32>(a, bk, s);
+  return kv_permuted ? dispatch_bk<D, BQ, false, PERM_QO, OUT32>(a, bk, s)
+                     : dispatch_bk<D, BQ, false, PERM_ALL, OUT32>(a, bk, s);
 }
 
 // Launch for one head dimension D (one translation unit per D).
@@ -67,11 +76,11 @@ hipError_t launch_d(const Geometry& g, const void* q, const void* k, const void*
   a.c = g.sm_scale * 1.4426950408889634f;
   const bool p = perm != nullptr;
   if (out_fp32) {
-    return g.block_q == 128 ? dispatch_mode<D, 128, true>(a, g.block_k, dense, p, s)
-                            : dispatch_mode<D, 64, true>(a, g.block_k, dense, p, s);
+    return g.block_q == 128 ? dispatch_mode<D, 128, true>(a, g.block_k, dense, p, g.kv_permuted, s)
+                            : dispatch_mode<D, 64, true>(a, g.block_k, dense, p, g.kv_permuted, s);
   }
-  return g.block_q == 128 ? dispatch_mode<D, 128, false>(a, g.block_k, dense, p, s)
-                          : dispatch_mode<D, 64, false>(a, g.block_k, dense, p, s);
+  return g.block_q == 128 ? dispatch_mode<D, 128, false>(a, g.block_k, dense, p, g.kv_permuted, s)
+                          : dispatch_mode<D, 64, false>(a, g.block_k, dense, p, g.kv_permuted, s);
 }
 
 }  // namespace attend_bf16_impl

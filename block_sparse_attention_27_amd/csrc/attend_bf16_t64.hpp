@@ -165,9 +165,11 @@ __device__ __forceinline__ float tile_xmax64(const f32x16 (&S)[2], const TileMet
   return fmaf(fmaxf(m0, m1), c, m.lw[0]);
 }
 
-template <int D, int BK, bool DENSE, bool PERM, bool OUT32>
+template <int D, int BK, bool DENSE, int PM, bool OUT32>
 __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) {
   constexpr int NT = 64 * NW64;
+  constexpr bool PERM = PM == PERM_ALL;  // K and V rows gathered through perm while staging
+  constexpr bool PQ = PM != PERM_NONE;   // Q rows gathered, out and lse rows scattered
   constexpr int SL = BK < T64 ? BK : T64;  // keys per slot of a tile
   constexpr int TB = T64 * 2 * D;          // bytes per staged tile
   using SG = StageGeom<D, NW64, T64>;
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
   // Q^T fragments (B operand): lane (row n, half h) holds d = 16 s + 8 h .. +7.
   const int qrow = qi * 128 + 32 * wave + n;
   bool qok = qrow < a.N;
-  const int qg = gather_row<PERM>(a, qrow, qok);
+  const int qg = gather_row<PQ>(a, qrow, qok);
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
   int orow = qrow;
   float inv = 0.f;
   if (qrow < a.N) {
-    orow = gather_row<PERM>(a, qrow, ok);
+    orow = gather_row<PQ>(a, qrow, ok);
     inv = lsum > 0.f ? 1.f / lsum : 0.f;
   }
   if constexpr (OUT32) {
@@ -480,7 +482,7 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
       const int grow = qi * 128 + 32 * wave + rr;  // this lane's query row
       bool rok = true;
       int orow_r = grow;
-      if (grow < a.N) orow_r = gather_row<PERM>(a, grow, rok);
+      if (grow < a.N) orow_r = gather_row<PQ>(a, grow, rok);
       const float4 x = *reinterpret_cast<const float4*>(stage + rr * (4 * D) + 16 * (c ^ (rr % CPR)));
       if (rok) *reinterpret_cast<float4*>(static_cast<float*>(a.out) + bh_off + static_cast<size_t>(orow_r) * D + 4 * c) = x;
     }

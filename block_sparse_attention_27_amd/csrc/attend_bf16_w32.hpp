@@ -34,8 +34,10 @@ __device__ __forceinline__ float tile_xmax_half(const f32x16 (&S)[2], const Tile
   return fmaxf(fmaf(m0, c, lw[0]), fmaf(m1, c, lw[1]));
 }
 
-template <int D, int BQ, int BK, bool DENSE, bool PERM, bool OUT32>
+template <int D, int BQ, int BK, bool DENSE, int PM, bool OUT32>
 __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
+  constexpr bool PERM = PM == PERM_ALL;  // K and V rows gathered through perm while staging
+  constexpr bool PQ = PM != PERM_NONE;   // Q rows gathered, out and lse rows scattered
   constexpr int NRG = BQ / 32;  // row groups
   constexpr int NW = 2 * NRG;   // waves: row group x key half
   constexpr int NT = 64 * NW;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
   // Q^T fragments (B operand): lane (row n, half h) holds d = 16 s + 8 h .. +7.
   const int qrow = qi * BQ + 32 * rg + n;
   bool qok = qrow < a.N;
-  const int qg = gather_row<PERM>(a, qrow, qok);
+  const int qg = gather_row<PQ>(a, qrow, qok);
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
   int orow = qrow;
   float inv = 0.f;
   if (qrow < a.N) {
-    orow = gather_row<PERM>(a, qrow, ok);
+    orow = gather_row<PQ>(a, qrow, ok);
     inv = lsum > 0.f ? 1.f / lsum : 0.f;
   }
   if (ok) {  // rows >= N (inv = 0) are written as zeros

@@ -86,6 +86,14 @@ __device__ __forceinline__ void pin(T& x) { asm volatile("" : "+v"(x)); }
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// How a kernel uses the permutation: not at all; to gather Q, K and V rows
+// and scatter the output rows; or, for K and V that arrive already in
+// permuted order (or dense attention, where the key order does not matter),
+// to gather the Q rows and scatter the output rows only.
+constexpr int PERM_NONE = 0;
+constexpr int PERM_ALL = 1;
+constexpr int PERM_QO = 2;
+
 template <bool PERM>
 __device__ __forceinline__ int gather_row(const AttendArgs& a, int r, bool& ok) {
   if constexpr (PERM) {

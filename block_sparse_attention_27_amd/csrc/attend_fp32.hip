@@ -29,7 +29,8 @@ struct Fp32Args {
   float* out;
   float* lse;
   int N, N_pad, nQB, nKU, L, block_k, n_wg;
-  float c;  // sm_scale * log2(e)
+  int kv_gather;  // 1: key rows go through perm as well (the sparse pass on K and V in token order)
+  float c;        // sm_scale * log2(e)
 };
 
 template <bool PERM>
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(BQ) void attend_fp32_kernel(Fp32Args a) {
     for (int x = tid; x < SEG * D; x += BQ) {
       const int r = x / D, col = x % D;
       bool ok = r < cnt;
-      const int g = row_of<PERM>(a, base + r, ok);
+      const int g = a.kv_gather ? row_of<PERM>(a, base + r, ok) : base + r;
       ks[r][col] = ok ? kb[static_cast<size_t>(g) * D + col] : 0.f;
       vs[r][col] = ok ? vb[static_cast<size_t>(g) * D + col] : 0.f;
     }
@@ -174,6 +175,8 @@ hipError_t launch_attend_fp32(const Geometry& g, const void* q, const void* k, c
   a.n_wg = g.B * g.H * g.nQB;
   a.c = g.sm_scale * 1.4426950408889634f;
   const bool dense = idx == nullptr, p = perm != nullptr;
+  // dense attention takes every valid key, in whatever order: no key gather
+  a.kv_gather = p && !dense && !g.kv_permuted;
   if (g.d == 128) return g.block_q == 128 ? dispatch<128, 128>(a, dense, p, s) : dispatch<128, 64>(a, dense, p, s);
   return g.block_q == 128 ? dispatch<64, 128>(a, dense, p, s) : dispatch<64, 64>(a, dense, p, s);
 }

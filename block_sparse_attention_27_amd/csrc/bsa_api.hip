@@ -16,7 +16,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Shape checks shared by all calls; fills the geometry.
 bsa_status check_problem(const bsa_problem* p, bsa::Geometry* g) {
   if (p == nullptr) return BSA_ERR_INVALID_ARG;
-  if (p->reserved != 0) return BSA_ERR_INVALID_ARG;
+  if (p->kv_permuted != 0 && p->kv_permuted != 1) return BSA_ERR_INVALID_ARG;
   if (p->B < 1 || p->H < 1 || p->N < 1 || p->N_pad < p->N) return BSA_ERR_INVALID_ARG;
   if (p->d != 64 && p->d != 128) return BSA_ERR_INVALID_ARG;
   if (p->block_q != 64 && p->block_q != 128) return BSA_ERR_INVALID_ARG;
@@ -43,6 +43,7 @@ bsa_status check_problem(const bsa_problem* p, bsa::Geometry* g) {
   g->L = 0;
   g->bf16 = p->dtype == BSA_BF16;
   g->out_fp32 = p->out_fp32 == 1;
+  g->kv_permuted = p->kv_permuted == 1;
   g->sm_scale = p->sm_scale;
   g->seed = p->seed;
   return BSA_OK;
@@ -55,6 +56,13 @@ bsa_status check_budget(const bsa_problem* p, bsa::Geometry* g) {
   if (L < 1 || L > g->n_valid_units) return BSA_ERR_INVALID_ARG;
   g->L = static_cast<int>(L);
   return BSA_OK;
+}
+
+// Calls that take a permutation: kv_permuted = 1 describes K and V gathered
+// by one, so it needs one.
+bool perm_ok(const bsa::Geometry& g, const int32_t* perm) {
+  if (perm && !aligned(perm, 4)) return false;
+  return perm != nullptr || !g.kv_permuted;
 }
 
 bsa_status from_hip(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
@@ -94,7 +102,7 @@ bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const i
   if (!q || !k || !S || !q_mean || !k_mean) return BSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(S, 4) || !aligned(q_mean, 16) || !aligned(k_mean, 16))
     return BSA_ERR_INVALID_ARG;
-  if (perm && !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
+  if (!perm_ok(g, perm)) return BSA_ERR_INVALID_ARG;
   st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, nullptr, false, stream));
   if (st != BSA_OK) return st;
   return from_hip(bsa::launch_scores(g, 1, q_mean, nullptr, k_mean, nullptr, S, stream));
@@ -109,7 +117,7 @@ bsa_status bsa_score_stats(const bsa_problem* p, const void* q, const void* k, c
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(S, 4) || !aligned(q_mean, 16) || !aligned(k_mean, 16) ||
       !aligned(k_var, 16))
     return BSA_ERR_INVALID_ARG;
-  if (perm && !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
+  if (!perm_ok(g, perm)) return BSA_ERR_INVALID_ARG;
   st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, k_var, false, stream));
   if (st != BSA_OK) return st;
   return from_hip(bsa::launch_scores(g, 1, q_mean, nullptr, k_mean, k_var, S, stream));
@@ -127,12 +135,31 @@ bsa_status bsa_score_ibcs(const bsa_problem* p, int32_t groups, int32_t iters, c
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(S, 4) || !aligned(q_cent, 16) || !aligned(q_size, 4) ||
       !aligned(k_mean, 16))
     return BSA_ERR_INVALID_ARG;
-  if (perm && !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
+  if (!perm_ok(g, perm)) return BSA_ERR_INVALID_ARG;
   st = from_hip(bsa::launch_block_means(g, q, k, perm, nullptr, k_mean, nullptr, true, stream));
   if (st != BSA_OK) return st;
   st = from_hip(bsa::launch_block_clusters(g, groups, iters, q, perm, q_cent, q_size, stream));
   if (st != BSA_OK) return st;
   return from_hip(bsa::launch_scores(g, groups, q_cent, q_size, k_mean, nullptr, S, stream));
+}
+
+bsa_status bsa_permute_rows(const bsa_problem* p, const void* x, const int32_t* perm, void* x_perm,
+                            hipStream_t stream) {
+  bsa::Geometry g;
+  bsa_status st = check_problem(p, &g);
+  if (st != BSA_OK) return st;
+  if (!x || !perm || !x_perm) return BSA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(x_perm, 16) || !aligned(perm, 4)) return BSA_ERR_INVALID_ARG;
+  const int64_t row_bytes = static_cast<int64_t>(g.d) * (g.bf16 ? 2 : 4);
+  const int64_t bytes = static_cast<int64_t>(g.B) * g.H * g.N_pad * row_bytes;
+  const uintptr_t xs = reinterpret_cast<uintptr_t>(x), ys = reinterpret_cast<uintptr_t>(x_perm);
+  if (xs < ys + static_cast<uintptr_t>(bytes) && ys < xs + static_cast<uintptr_t>(bytes)) return BSA_ERR_INVALID_ARG;
+  // the kernel indexes the 16-byte chunks of one (b, h) in int32, and the grid
+  // (1024 chunks per 256-thread workgroup) must stay within 2^32 work-items
+  const int64_t chunks = static_cast<int64_t>(g.N_pad) * (row_bytes / 16);
+  if (chunks > 0x7FFFFFFFll - 1024) return BSA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(g.B) * g.H * ((chunks + 1023) / 1024) * 256 > 0xFFFFFFFFll) return BSA_ERR_UNSUPPORTED;
+  return from_hip(bsa::launch_permute_rows(g, x, perm, x_perm, stream));
 }
 
 bsa_status bsa_select(const bsa_problem* p, const float* S, int32_t* idx, float* w, hipStream_t stream) {
@@ -157,7 +184,7 @@ bsa_status bsa_attend(const bsa_problem* p, const void* q, const void* k, const 
   if (st != BSA_OK) return st;
   if (!q || !k || !v || !idx || !w || !out) return BSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
-      !aligned(w, 4) || (lse && !aligned(lse, 4)) || (perm && !aligned(perm, 4)))
+      !aligned(w, 4) || (lse && !aligned(lse, 4)) || !perm_ok(g, perm))
     return BSA_ERR_INVALID_ARG;
   if (g.bf16) return from_hip(bsa::launch_attend_bf16(g, q, k, v, perm, idx, w, out, lse, stream));
   return from_hip(bsa::launch_attend_fp32(g, q, k, v, perm, idx, w, out, lse, stream));
@@ -170,7 +197,7 @@ bsa_status bsa_attend_dense(const bsa_problem* p, const void* q, const void* k, 
   if (st != BSA_OK) return st;
   if (!q || !k || !v || !out) return BSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-      (lse && !aligned(lse, 4)) || (perm && !aligned(perm, 4)))
+      (lse && !aligned(lse, 4)) || !perm_ok(g, perm))
     return BSA_ERR_INVALID_ARG;
   if (g.bf16) return from_hip(bsa::launch_attend_bf16(g, q, k, v, perm, nullptr, nullptr, out, lse, stream));
   return from_hip(bsa::launch_attend_fp32(g, q, k, v, perm, nullptr, nullptr, out, lse, stream));

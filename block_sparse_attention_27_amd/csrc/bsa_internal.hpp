@@ -12,6 +12,7 @@ struct Geometry {
   int nQB, nKU, n_valid_units, L;
   bool bf16;
   bool out_fp32;  // bf16 inputs with an fp32 output
+  bool kv_permuted;  // K and V rows arrive in permuted order (only Q and out go through perm)
   float sm_scale;
   uint64_t seed;
 };
@@ -29,6 +30,11 @@ hipError_t launch_scores(const Geometry& g, int groups, const float* q_rep, cons
 // k-means of every query block's valid rows: `groups` centroids and row counts
 hipError_t launch_block_clusters(const Geometry& g, int groups, int iters, const void* q,
                                  const int32_t* perm, float* q_cent, int32_t* q_size, hipStream_t s);
+
+// ---- permutation ----
+// x_perm[b][h][r] = x[b][h][perm[r]] for r < N (a zero row for an entry
+// outside [0, N_pad)); rows N .. N_pad-1 of x_perm are zero
+hipError_t launch_permute_rows(const Geometry& g, const void* x, const int32_t* perm, void* x_perm, hipStream_t s);
 
 // ---- selection ----
 hipError_t launch_select(const Geometry& g, int k_exact, int m_sample, const float* S, int32_t* idx,

@@ -45,6 +45,7 @@ struct MeansArgs {
   float* k_mean;
   float* k_var;  // nullptr, or per-dimension population variance of every key unit
   int N, N_pad, block_q, block_k, nQB, nKU, n_bh;
+  int k_gather;  // 1: key rows go through perm too (0: K arrives in permuted order)
   int first;  // logical block of workgroup 0 (n_bh * nQB: key units only)
 };
 
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(MEAN_THREADS) void block_means_kernel(MeansArgs a) 
     bool ok = r < nvalid;
     int g = row0 + r;
     if constexpr (PERM) {
-      if (ok) {
+      if (ok && (is_q || a.k_gather)) {
         g = a.perm[g];
         ok = static_cast<unsigned>(g) < static_cast<unsigned>(a.N_pad);
       }
@@ -732,6 +733,7 @@ hipError_t launch_block_means(const Geometry& g, const void* q, const void* k, c
   a.first = keys_only ? a.n_bh * g.nQB : 0;
   const dim3 grid(a.n_bh * ((keys_only ? 0 : g.nQB) + g.nKU));
   const bool p = perm != nullptr;
+  a.k_gather = p && !g.kv_permuted;
 #define BSA_MEANS(D, BF, P) hipLaunchKernelGGL((block_means_kernel<D, BF, P>), grid, dim3(MEAN_THREADS), 0, s, a)
   if (g.d == 128) {
     if (g.bf16) { if (p) BSA_MEANS(128, true, true); else BSA_MEANS(128, true, false); }

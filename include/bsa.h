@@ -33,7 +33,11 @@
  *              perm[r] of out (and lse). perm must map 0..N-1 onto 0..N-1;
  *              entries r >= N are not read. An entry outside [0, N_pad) is
  *              never dereferenced (no out-of-bounds access) but the result is
- *              then unspecified.
+ *              then unspecified. With kv_permuted = 1 the caller passes K and
+ *              V already gathered (K' and V', as bsa_permute_rows writes
+ *              them) and only Q and out go through perm; the results are the
+ *              same, and the sparse pass reads each key unit as one run of
+ *              contiguous rows instead of gathering it row by row.
  *   Memory     All array arguments are device pointers owned by the caller;
  *              Q/K/V/out must be 16-byte aligned, the others 4-byte aligned.
  *              The library allocates nothing, keeps no state between calls and
@@ -55,7 +59,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 4
+#define BSA_ABI_VERSION 5
 
 typedef enum bsa_status {
   BSA_OK = 0,
@@ -82,7 +86,8 @@ typedef struct bsa_problem {
   int32_t m_sample;   /* sample size m >= 0; 1 <= k+m <= number of valid units */
   int32_t dtype;      /* bsa_dtype of Q, K, V */
   int32_t out_fp32;   /* 0: out has the element type of Q; 1: out is fp32 (always fp32 for BSA_FP32) */
-  int32_t reserved;   /* must be 0 */
+  int32_t kv_permuted; /* 0: K and V in token order; 1: K and V given as K' = K[perm],
+                          V' = V[perm] (needs perm in every call that takes one) */
   uint64_t seed;      /* sampler seed (Philox4x32-10 key) */
   float sm_scale;     /* logit = sm_scale * <q, k>; finite and > 0 */
 } bsa_problem;
@@ -189,6 +194,20 @@ bsa_status bsa_score_stats(const bsa_problem* p, const void* q, const void* k, c
  */
 bsa_status bsa_select(const bsa_problem* p, const float* S, int32_t* idx, float* w,
                       hipStream_t stream);
+
+/*
+ * bsa_permute_rows -- x_perm[b][h][r] = x[b][h][perm[r]] for r < N; rows
+ * N .. N_pad-1 of x_perm are written as zeros, and so is a row whose perm
+ * entry lies outside [0, N_pad).
+ * (InstaGen, Abstract: permuted block-sparse attention computes blocks of an
+ * attention matrix whose tokens have been reordered by semantic similarity.)
+ * Puts K and V into the permuted order once, for calls with kv_permuted = 1.
+ * x and x_perm are [B][H][N_pad][d] of `dtype`, 16-byte aligned, and must not
+ * overlap; perm is required. Uses B, H, N, N_pad, d and dtype of p. A pure
+ * copy of bytes: bit-exact.
+ */
+bsa_status bsa_permute_rows(const bsa_problem* p, const void* x, const int32_t* perm, void* x_perm,
+                            hipStream_t stream);
 
 /*
  * bsa_attend -- one weighted block-sparse attention pass.

@@ -32,8 +32,8 @@ def _declared_functions():
 
 def test_header_declares_the_pipeline():
     names = _declared_functions()
-    for n in ("bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_attend", "bsa_attend_dense",
-              "bsa_status_string", "bsa_abi_version"):
+    for n in ("bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_permute_rows", "bsa_attend",
+              "bsa_attend_dense", "bsa_status_string", "bsa_abi_version"):
         assert n in names
 
 
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 4
+    assert lib.bsa_abi_version() == 5
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(1) == b"invalid argument"
     assert lib.bsa_status_string(99) == b"unknown status"
@@ -62,20 +62,20 @@ def test_problem_struct_layout_matches_header(tmp_path):
     src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "bsa.h"\n'
                    'int main(void){printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(bsa_problem),'
                    ' offsetof(bsa_problem, dtype), offsetof(bsa_problem, seed),'
-                   ' offsetof(bsa_problem, sm_scale), offsetof(bsa_problem, reserved),'
+                   ' offsetof(bsa_problem, sm_scale), offsetof(bsa_problem, kv_permuted),'
                    ' offsetof(bsa_problem, out_fp32)); return 0;}\n')
     exe = tmp_path / "layout"
     subprocess.run([gcc, "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
                     "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
     c_vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     P = bsa.Problem
-    assert c_vals == [ctypes.sizeof(P), P.dtype.offset, P.seed.offset, P.sm_scale.offset, P.reserved.offset,
+    assert c_vals == [ctypes.sizeof(P), P.dtype.offset, P.seed.offset, P.sm_scale.offset, P.kv_permuted.offset,
                       P.out_fp32.offset]
 
 
 def _good(**kw):
     f = dict(B=1, H=2, N=1000, N_pad=1024, d=128, block_q=128, block_k=64, k_exact=2, m_sample=3,
-             dtype=bsa.BSA_BF16, out_fp32=0, seed=1, sm_scale=1.0, reserved=0)
+             dtype=bsa.BSA_BF16, out_fp32=0, seed=1, sm_scale=1.0, kv_permuted=0)
     f.update(kw)
     return bsa.Problem(**f)
 
@@ -83,7 +83,8 @@ def _good(**kw):
 BAD = [
     dict(B=0), dict(H=0), dict(N=0), dict(N=2000), dict(d=96), dict(block_q=32), dict(block_k=16),
     dict(N_pad=1000), dict(dtype=7), dict(sm_scale=0.0), dict(sm_scale=float("inf")),
-    dict(sm_scale=float("nan")), dict(reserved=1), dict(N_pad=1 << 29, N=1 << 29), dict(out_fp32=2),
+    dict(sm_scale=float("nan")), dict(kv_permuted=2), dict(kv_permuted=-1), dict(N_pad=1 << 29, N=1 << 29),
+    dict(out_fp32=2),
 ]
 BAD_BUDGET = [dict(k_exact=-1), dict(m_sample=-1), dict(k_exact=0, m_sample=0),
               dict(k_exact=10, m_sample=7)]  # 16 valid units of 64 keys in N = 1000
@@ -101,6 +102,34 @@ def test_invalid_problem_rejected_by_every_call(lib, bad):
     assert lib.bsa_select(p, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_attend(p, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_attend_dense(p, FAKE, FAKE, FAKE, None, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_permute_rows(p, FAKE, FAKE, ctypes.c_void_p(0x7E0000000000), None) == bsa.BSA_ERR_INVALID_ARG
+
+
+def test_kv_permuted_needs_a_permutation(lib):
+    p = ctypes.byref(_good(kv_permuted=1))
+    assert lib.bsa_score(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_score_ibcs(p, 4, 3, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_score_stats(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_attend(p, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_attend_dense(p, FAKE, FAKE, FAKE, None, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
+
+
+def test_permute_rows_argument_checks(lib):
+    p = ctypes.byref(_good())
+    other = ctypes.c_void_p(0x7E0000000000)
+    bytes_ = 1 * 2 * 1024 * 128 * 2
+    # null pointers, missing permutation, misalignment
+    assert lib.bsa_permute_rows(p, None, FAKE, other, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_permute_rows(p, FAKE, None, other, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_permute_rows(p, FAKE, FAKE, None, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_permute_rows(p, ctypes.c_void_p(0x7F0000000008), FAKE, other, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_permute_rows(p, FAKE, ctypes.c_void_p(0x7F0000000002), other, None) == bsa.BSA_ERR_INVALID_ARG
+    # in place and overlapping buffers
+    assert lib.bsa_permute_rows(p, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_permute_rows(p, FAKE, FAKE, ctypes.c_void_p(0x7F0000000000 + bytes_ - 16),
+                                None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_permute_rows(p, FAKE, FAKE, ctypes.c_void_p(0x7F0000000000 - bytes_ + 16),
+                                None) == bsa.BSA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("groups,iters", [(0, 3), (3, 3), (16, 3), (-1, 3), (4, 0), (4, 17), (4, -2)])

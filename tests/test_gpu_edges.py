@@ -94,7 +94,11 @@ def test_dense_limit_matches_dense_kernel(dtype):
     assert np.all(wt.cpu().numpy() == 1.0)
     p32 = bsa.Problem.from_buffer_copy(p)
     p32.out_fp32 = 1
-    outd = bsa.attend_dense(p32, q, k, v, perm)
+    # dense attention reads the keys in the order it is given them; on K' and V'
+    # it meets them in the sparse pass's order (units ascending), so the two
+    # round P to bf16 over the same tiles
+    kp, vp = bsa.permute_rows(p, k, perm), bsa.permute_rows(p, v, perm)
+    outd = bsa.attend_dense(bsa.with_kv_permuted(p32), q, kp, vp, perm)
     torch.cuda.synchronize()
     a, b = to_f64(out), to_f64(outd)
     assert rel_l2(a, b) <= 2e-3 and np.max(np.abs(a - b)) <= 1e-2
@@ -182,7 +186,7 @@ def test_selection_hostile_rows_bitexact(n_valid, k, m):
     H = 1
     rows_cap = 64 if n_valid > 1000 else 400
     p = bsa.Problem(B=1, H=H, N=N, N_pad=N_pad, d=128, block_q=128, block_k=bk, k_exact=k, m_sample=m,
-                    dtype=bsa.BSA_BF16, seed=0xDEADBEEF12345678, sm_scale=1.0, reserved=0)
+                    dtype=bsa.BSA_BF16, seed=0xDEADBEEF12345678, sm_scale=1.0, kv_permuted=0)
     rng = np.random.default_rng(n_valid)
     S = _hostile_rows(nqb, n_valid, n_units, rng).reshape(1, H, nqb, n_units)
     idx, wt = bsa.select(p, torch.from_numpy(S).cuda())

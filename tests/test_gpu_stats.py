@@ -52,7 +52,7 @@ def test_stats_identical_keys_match_plain_scorer():
     q[..., N:, :] = 0
     k[..., N:, :] = 0
     p = bsa.Problem(B=B, H=H, N=N, N_pad=Np, d=d, block_q=128, block_k=bk, k_exact=1, m_sample=1,
-                    dtype=bsa.BSA_FP32, out_fp32=0, seed=0, sm_scale=1.0, reserved=0)
+                    dtype=bsa.BSA_FP32, out_fp32=0, seed=0, sm_scale=1.0, kv_permuted=0)
     qd, kd = to_device(q), to_device(k)
     S1, _, _, kv = bsa.score_stats(p, qd, kd)
     S0, _, _ = bsa.score(p, qd, kd)
