@@ -214,6 +214,9 @@ __device__ __forceinline__ uint64_t block_exscan(uint64_t v, BlockRed& r, int& p
   return before + x - v;
 }
 
+// ceil(x / d) for d >= 1: the smallest q with d q >= x.
+__device__ __forceinline__ uint32_t level(uint32_t x, uint32_t d) { return x / d + (x % d != 0u ? 1u : 0u); }
+
 // The threshold search of the exact set runs in two phases: the top bits
 // 30..SPLIT over every key, then the low SPLIT bits over the keys that share
 // the threshold's top bits ("in play"), compacted into LDS. For the largest
@@ -253,14 +256,14 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
   }
   __syncthreads();
 
-  // Per-unit state stays small (three waves per SIMD at 135 registers was
-  // the limit before): validity is recomputed from the unit index, the exact
-  // set and the capped units are bit masks (bit e: unit tid E + e), and pi
-  // (1 <= pi <= 2^32 on R) is held as pi - 1 in 32 bits.
+  // Per-unit state stays small: validity is recomputed from the unit index,
+  // the exact set is a bit mask (bit e: unit tid E + e), the capped units are
+  // the units of R at or above the water level, and pi (1 <= pi <= 2^32 on R)
+  // is held as pi - 1 in 32 bits.
   const int j0 = tid * E;
   auto valid = [&](int e) { return j0 + e < a.nV; };
   uint32_t key[E];
-  uint32_t fK = 0, fcap = 0;
+  uint32_t fK = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) key[e] = valid(e) ? sanitize(sbits[j0 + e]) : 0u;
 
@@ -349,117 +352,129 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
       }
     }
   }
-  auto inK = [&](int e) { return ((fK >> e) & 1u) != 0u; };
-  auto inR = [&](int e) { return valid(e) && !inK(e); };
-  auto capped = [&](int e) { return ((fcap >> e) & 1u) != 0u; };
+  auto inR = [&](int e) { return valid(e) && ((fK >> e) & 1u) == 0u; };
 
+  // ---- 2. inclusion probabilities on R (valid and not in K) ----
+  // q: quantised scores on R, 1 <= q < 2^FS, and 0 elsewhere, so that with at
+  // most 4096 valid units every sum of q fits 32 bits. thr: the water level;
+  // the capped units (pi = 1) are the units of R with q >= thr.
+  uint32_t q[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) q[e] = 0u;
+  uint32_t thr = 0xFFFFFFFFu, delta = 0;
   uint32_t pim1[E];  // pi - 1 on R (pi in [1, 2^32])
-  uint64_t delta = 0;
   if (a.m > 0) {
     // ---- 2a. quantised scores over R ----
     uint32_t mx = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (inR(e)) mx = max(mx, key[e]);
+    for (int e = 0; e < E; ++e) mx = max(mx, inR(e) ? key[e] : 0u);
     mx = block_max(mx, red, par);
-    uint32_t q[E];
     const int ex = mx ? frexp_exp(mx) : 0;
-    uint64_t qsum = 0;
+    uint32_t qsum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       q[e] = inR(e) ? (mx ? quantise(key[e], ex) : 1u) : 0u;
       qsum += q[e];
     }
-    uint64_t QU = block_sum(qsum, red, par);
+    const uint32_t QR = block_sum(qsum, red, par);
 
     // ---- 2b. water-filling on exact integers ----
-    uint64_t t = 0;
+    // A unit of R is capped once (m - t) q_j >= Q_U, i.e. once q_j reaches the
+    // level ceil(Q_U / (m - t)), with t the capped units and Q_U the sum of q
+    // over the others. Capping the units at or above the level can only lower
+    // it, so after every round the capped units are exactly those with q at or
+    // above the current level: a round is one compare per unit and one sum,
+    // until a round caps nothing new.
+    uint32_t t = 0, QU = QR;
+    thr = level(QU, static_cast<uint32_t>(a.m));
     while (true) {
-      const uint64_t mt = static_cast<uint64_t>(a.m) - t;
-      uint64_t packed = 0;  // (count << 40) | sum of q
+      uint32_t cnt = 0, qs = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        if (inR(e) && !capped(e) && mt * q[e] >= QU) {
-          fcap |= 1u << e;
-          packed += (1ull << 40) + q[e];
-        }
+        const bool cap = q[e] >= thr;  // q = 0 outside R never reaches thr >= 1
+        cnt += cap ? 1u : 0u;
+        qs += cap ? q[e] : 0u;
       }
-      packed = block_sum(packed, red, par);
-      const uint64_t cnt = packed >> 40;
-      if (cnt == 0) break;
-      t += cnt;
-      QU -= packed & ((1ull << 40) - 1);
+      const uint64_t tot = block_sum((static_cast<uint64_t>(cnt) << 40) | qs, red, par);
+      const uint32_t nt = static_cast<uint32_t>(tot >> 40);
+      if (nt == t) break;
+      t = nt;
+      QU = QR - static_cast<uint32_t>(tot & ((1ull << 40) - 1));
+      if (t >= static_cast<uint32_t>(a.m)) break;  // R is all capped (t = m = |R|)
+      thr = level(QU, static_cast<uint32_t>(a.m) - t);
     }
 
     // ---- 2c. fixed-point pi ----
-    // (m - t) q_j < 2^33 and Q_U < 2^33 are exact in fp64, and so is their
-    // product form below; an uncapped unit has (m - t) q_j < Q_U, so its
-    // correctly rounded ratio is below 1 and 2^32 ratio fits 32 bits (>= 1).
-    const uint64_t mt = static_cast<uint64_t>(a.m) - t;
-    const double mt_d = static_cast<double>(static_cast<uint32_t>(mt));
-    const double qu_d = static_cast<double>(QU);
+    // (m - t) q_j < 2^32 and Q_U < 2^32 are exact in fp64; an uncapped unit has
+    // (m - t) q_j < Q_U, so its correctly rounded ratio is below 1 and 2^32
+    // ratio fits 32 bits (>= 1).
+    const uint32_t mt = static_cast<uint32_t>(a.m) - t;
+    const double mt_d = static_cast<double>(mt), qu_d = static_cast<double>(QU);
     uint64_t usum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       pim1[e] = 0xFFFFFFFFu;  // capped: pi = 2^32
-      if (inR(e) && !capped(e)) {
+      if (q[e] != 0u && q[e] < thr) {
         const double ratio = (mt_d * static_cast<double>(q[e])) / qu_d;
         const uint32_t pv = static_cast<uint32_t>(ratio * 4294967296.0);
         pim1[e] = pv - 1u;
         usum += pv;
       }
     }
-    delta = (mt << 32) - block_sum(usum, red, par);
+    // below the number of uncapped units: the floors lose less than 1 each
+    delta = static_cast<uint32_t>((static_cast<uint64_t>(mt) << 32) - block_sum(usum, red, par));
   }
 
   // ---- ranks in unit order: K (high word) and uncapped R (low word) ----
-  uint32_t nk = 0, nu = 0;
+  uint32_t nu = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    nk += inK(e) ? 1u : 0u;
-    nu += (inR(e) && !capped(e)) ? 1u : 0u;
-  }
+  for (int e = 0; e < E; ++e) nu += (q[e] != 0u && q[e] < thr) ? 1u : 0u;
   uint64_t rk_total;
-  const uint64_t rk = block_exscan((static_cast<uint64_t>(nk) << 32) | nu, red, par, rk_total);
-  uint32_t kpos = static_cast<uint32_t>(rk >> 32);
-  uint32_t upos = static_cast<uint32_t>(rk);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = j0 + e;
-    if (inK(e)) {
-      irow[kpos] = j;
+  const uint64_t rk = block_exscan((static_cast<uint64_t>(__popc(fK)) << 32) | nu, red, par, rk_total);
+  {  // the exact set, ascending, with w = 1
+    uint32_t kpos = static_cast<uint32_t>(rk >> 32);
+    for (uint32_t f = fK; f != 0u; f &= f - 1u, ++kpos) {
+      irow[kpos] = j0 + __builtin_ctz(f);
       wrow[kpos] = 1.0f;
-      ++kpos;
-    }
-    if (a.m > 0 && inR(e) && !capped(e)) {
-      if (upos < delta) pim1[e] += 1u;
-      ++upos;
     }
   }
 
   if (a.m > 0) {
-    // ---- 3. systematic sample over the cumulative pi axis ----
+    // the shortfall delta as +1 to the first delta uncapped units, then the
+    // sum of pi over this thread's units of R
+    uint32_t upos = static_cast<uint32_t>(rk);
     uint64_t psum = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (inR(e)) psum += static_cast<uint64_t>(pim1[e]) + 1u;
+    for (int e = 0; e < E; ++e) {
+      const bool unc = q[e] != 0u && q[e] < thr;
+      pim1[e] += (unc && upos < delta) ? 1u : 0u;
+      upos += unc ? 1u : 0u;
+      psum += q[e] != 0u ? static_cast<uint64_t>(pim1[e]) + 1u : 0u;
+    }
+
+    // ---- 3. systematic sample over the cumulative pi axis: slot s sits at
+    // u + s 2^32. This thread's units cover [c, c + psum); np is the first slot
+    // at or above the running end c, and since pi <= 2^32 a unit holds at most
+    // one slot (units outside R add nothing and hold none) ----
     uint64_t ptotal;
     uint64_t c = block_exscan(psum, red, par, ptotal);
     const uint64_t u = philox_word0(static_cast<uint32_t>(i), static_cast<uint32_t>(hd),
                                     static_cast<uint32_t>(b), 0u, a.seed_lo, a.seed_hi);
-    auto below = [u](uint64_t x) -> uint64_t { return x > u ? ((x - u - 1) >> 32) + 1 : 0; };
+    uint32_t n = c > u ? static_cast<uint32_t>(((c - u - 1) >> 32) + 1) : 0u;  // slots below c
+    uint64_t np = u + (static_cast<uint64_t>(n) << 32);
     // every key is in registers and the exscan's barrier has passed: the
     // staging array hands pi - 1 of each sampled slot (1 <= pi <= 2^32) to the
     // thread that writes its weight (k + m <= nV slots)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (!inR(e)) continue;
-      const uint64_t c0 = c;
-      c += static_cast<uint64_t>(pim1[e]) + 1u;
-      const uint64_t n0 = below(c0), n1 = below(c);
-      if (n1 > n0 && n0 < static_cast<uint64_t>(a.m)) {  // n0 < m always holds when sum pi = m 2^32
-        irow[a.k + static_cast<int>(n0)] = j0 + e;
-        sbits[n0] = pim1[e];
+      c += q[e] != 0u ? static_cast<uint64_t>(pim1[e]) + 1u : 0u;
+      if (c > np) {
+        if (n < static_cast<uint32_t>(a.m)) {  // always, when sum pi = m 2^32
+          irow[a.k + static_cast<int>(n)] = j0 + e;
+          sbits[n] = pim1[e];
+        }
+        ++n;
+        np += 1ull << 32;
       }
     }
     __syncthreads();
@@ -511,11 +526,12 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // Small per-unit state, as in select_kernel: validity from the unit index,
-  // bit masks for the exact set and the capped units, pi - 1 in 32 bits.
+  // a bit mask for the exact set, the water level for the capped units, pi - 1
+  // in 32 bits.
   const int j0 = lane * E;
   auto valid = [&](int e) { return j0 + e < a.nV; };
   uint32_t key[E];
-  uint32_t fK = 0, fcap = 0;
+  uint32_t fK = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t raw = sb[j0 + e];  // inside the wave's slice; ignored past nV
@@ -591,107 +607,96 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
       }
     }
   }
-  auto inK = [&](int e) { return ((fK >> e) & 1u) != 0u; };
-  auto inR = [&](int e) { return valid(e) && !inK(e); };
-  auto capped = [&](int e) { return ((fcap >> e) & 1u) != 0u; };
+  auto inR = [&](int e) { return valid(e) && ((fK >> e) & 1u) == 0u; };
 
+  // ---- 2. inclusion probabilities on R, as in select_kernel ----
+  uint32_t q[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) q[e] = 0u;
+  uint32_t thr = 0xFFFFFFFFu, delta = 0;
   uint32_t pim1[E];  // pi - 1 on R (pi in [1, 2^32])
-
-  uint64_t delta = 0;
   if (a.m > 0) {
     // ---- 2a. quantised scores over R ----
     uint32_t mx = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (inR(e)) mx = max(mx, key[e]);
+    for (int e = 0; e < E; ++e) mx = max(mx, inR(e) ? key[e] : 0u);
     mx = wave_max_u32(mx);
-    uint32_t q[E];
     const int ex = mx ? frexp_exp(mx) : 0;
-    uint64_t qsum = 0;
+    uint32_t qsum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       q[e] = inR(e) ? (mx ? quantise(key[e], ex) : 1u) : 0u;
       qsum += q[e];
     }
-    uint64_t QU = wave_sum(qsum);
+    const uint32_t QR = wave_sum(qsum);
 
-    // ---- 2b. water-filling on exact integers ----
-    uint64_t t = 0;
+    // ---- 2b. water-filling on exact integers: rounds of one compare per unit ----
+    uint32_t t = 0, QU = QR;
+    thr = level(QU, static_cast<uint32_t>(a.m));
     while (true) {
-      const uint64_t mt = static_cast<uint64_t>(a.m) - t;
-      uint64_t qcap = 0;
-      uint32_t cnt = 0;
+      uint32_t cnt = 0, qs = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool cap = inR(e) && !capped(e) && mt * q[e] >= QU;
+        const bool cap = q[e] >= thr;
         cnt += __popcll(__ballot(cap));
-        if (cap) {
-          fcap |= 1u << e;
-          qcap += q[e];
-        }
+        qs += cap ? q[e] : 0u;
       }
-      if (cnt == 0) break;
-      t += cnt;
-      QU -= wave_sum(qcap);
+      if (cnt == t) break;
+      t = cnt;
+      QU = QR - wave_sum(qs);
+      if (t >= static_cast<uint32_t>(a.m)) break;
+      thr = level(QU, static_cast<uint32_t>(a.m) - t);
     }
 
     // ---- 2c. fixed-point pi ----
-    // (m - t) q_j < 2^33 and Q_U < 2^31 are exact in fp64, and so is their
-    // product form below; an uncapped unit has (m - t) q_j < Q_U, so its
-    // correctly rounded ratio is below 1 and 2^32 ratio fits 32 bits.
-    const uint64_t mt = static_cast<uint64_t>(a.m) - t;
-    const double mt_d = static_cast<double>(static_cast<uint32_t>(mt));
-    const double qu_d = static_cast<double>(QU);
+    const uint32_t mt = static_cast<uint32_t>(a.m) - t;
+    const double mt_d = static_cast<double>(mt), qu_d = static_cast<double>(QU);
     uint64_t usum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       pim1[e] = 0xFFFFFFFFu;  // capped: pi = 2^32
-      if (inR(e) && !capped(e)) {
+      if (q[e] != 0u && q[e] < thr) {
         const double ratio = (mt_d * static_cast<double>(q[e])) / qu_d;
         const uint32_t pv = static_cast<uint32_t>(ratio * 4294967296.0);
         pim1[e] = pv - 1u;
         usum += pv;
       }
     }
-    delta = (mt << 32) - wave_sum(usum);
+    delta = static_cast<uint32_t>((static_cast<uint64_t>(mt) << 32) - wave_sum(usum));
   }
 
   // ---- ranks in unit order: K (high word) and uncapped R (low word) ----
-  uint32_t nk = 0, nu = 0;
+  uint32_t nu = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    nk += inK(e) ? 1u : 0u;
-    nu += (inR(e) && !capped(e)) ? 1u : 0u;
-  }
+  for (int e = 0; e < E; ++e) nu += (q[e] != 0u && q[e] < thr) ? 1u : 0u;
   uint64_t rk_total;
-  const uint64_t rk = wave_exscan((static_cast<uint64_t>(nk) << 32) | nu, rk_total);
-  uint32_t kpos = static_cast<uint32_t>(rk >> 32);
-  uint32_t upos = static_cast<uint32_t>(rk);
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = j0 + e;
-    if (inK(e)) {
-      irow[kpos] = j;
+  const uint64_t rk = wave_exscan((static_cast<uint64_t>(__popc(fK)) << 32) | nu, rk_total);
+  {
+    uint32_t kpos = static_cast<uint32_t>(rk >> 32);
+    for (uint32_t f = fK; f != 0u; f &= f - 1u, ++kpos) {
+      irow[kpos] = j0 + __builtin_ctz(f);
       wrow[kpos] = 1.0f;
-      ++kpos;
-    }
-    if (a.m > 0 && inR(e) && !capped(e)) {
-      if (upos < delta) pim1[e] += 1u;
-      ++upos;
     }
   }
 
   if (a.m > 0) {
-    // ---- 3. systematic sample over the cumulative pi axis ----
+    uint32_t upos = static_cast<uint32_t>(rk);
     uint64_t psum = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (inR(e)) psum += static_cast<uint64_t>(pim1[e]) + 1u;
+    for (int e = 0; e < E; ++e) {
+      const bool unc = q[e] != 0u && q[e] < thr;
+      pim1[e] += (unc && upos < delta) ? 1u : 0u;
+      upos += unc ? 1u : 0u;
+      psum += q[e] != 0u ? static_cast<uint64_t>(pim1[e]) + 1u : 0u;
+    }
+
+    // ---- 3. systematic sample over the cumulative pi axis ----
     uint64_t ptotal;
     uint64_t c = wave_exscan(psum, ptotal);
     const uint64_t u = philox_word0(static_cast<uint32_t>(i), static_cast<uint32_t>(hd),
                                     static_cast<uint32_t>(b), 0u, a.seed_lo, a.seed_hi);
-    auto below = [u](uint64_t x) -> uint64_t { return x > u ? ((x - u - 1) >> 32) + 1 : 0; };
+    uint32_t n = c > u ? static_cast<uint32_t>(((c - u - 1) >> 32) + 1) : 0u;
+    uint64_t np = u + (static_cast<uint64_t>(n) << 32);
     // every key is in registers now: the slice is reused to hand pi - 1 of
     // each sampled slot (1 <= pi <= 2^32) to the lane that writes its weight
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -699,13 +704,14 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      if (!inR(e)) continue;
-      const uint64_t c0 = c;
-      c += static_cast<uint64_t>(pim1[e]) + 1u;
-      const uint64_t n0 = below(c0), n1 = below(c);
-      if (n1 > n0 && n0 < static_cast<uint64_t>(a.m)) {  // k + m <= nV <= 64 E slots
-        irow[a.k + static_cast<int>(n0)] = j0 + e;
-        sb[n0] = pim1[e];
+      c += q[e] != 0u ? static_cast<uint64_t>(pim1[e]) + 1u : 0u;
+      if (c > np) {
+        if (n < static_cast<uint32_t>(a.m)) {  // k + m <= nV <= 64 E slots
+          irow[a.k + static_cast<int>(n)] = j0 + e;
+          sb[n] = pim1[e];
+        }
+        ++n;
+        np += 1ull << 32;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
