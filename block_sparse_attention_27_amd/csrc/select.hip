@@ -86,17 +86,19 @@ __device__ __forceinline__ int frexp_exp(uint32_t x) {
   return (32 - __clz(mant)) - 149;
 }
 
-// floor(value(x) 2^(FS - e)), at least 1; exact integer arithmetic.
+// floor(value(x) 2^(FS - e)), at least 1; exact integer arithmetic. Every x
+// is at most the maximum whose exponent is e, so value(x) < 2^e and the result
+// is below 2^FS: 32 bits hold it, and a left shift (x and the maximum both
+// subnormal) stays below 2^FS.
 __device__ __forceinline__ uint32_t quantise(uint32_t x, int e) {
   if (x == 0u) return 1u;
   const int E = static_cast<int>(x >> 23);
-  const uint64_t sig = E ? ((x & 0x007FFFFFu) | 0x00800000u) : (x & 0x007FFFFFu);
+  const uint32_t sig = E ? ((x & 0x007FFFFFu) | 0x00800000u) : (x & 0x007FFFFFu);
   const int shift = (E ? E : 1) - 150 + FS - e;
-  uint64_t q;
+  uint32_t q;
   if (shift >= 0) q = sig << shift;
-  else if (shift > -64) q = sig >> (-shift);
-  else q = 0;
-  return q > 0 ? static_cast<uint32_t>(q) : 1u;
+  else q = shift > -32 ? sig >> (-shift) : 0u;
+  return q > 0u ? q : 1u;
 }
 
 // Cross-lane steps on DPP moves, which stay in the VALU (a lane shuffle is an
@@ -225,8 +227,10 @@ __device__ __forceinline__ uint32_t level(uint32_t x, uint32_t d) { return x / d
 constexpr int SPLIT = 19;      // top 12 bits: the exponent and 4 mantissa bits
 constexpr int PLAY_MAX = 256;  // in-play keys one wave finishes (4 per lane); more take the block loop
 
+// Six waves per SIMD (at most 80 registers): the kernel is bound by vector
+// ALU issue, and more resident rows hide the latency of its barriers.
 template <int E>
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void select_kernel(SelectArgs a) {
   static_assert(PLAY_MAX <= SEL_THREADS * E, "the in-play keys borrow the row's staging array");
   __shared__ uint32_t sbits[SEL_THREADS * E];
   __shared__ BlockRed red;
@@ -248,11 +252,10 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(SelectArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int x = tid + e * SEL_THREADS;
-      v[e] = x < a.nV ? __float_as_uint(srow[x]) : 0u;
+      v[e] = __float_as_uint(srow[min(x, a.nV - 1)]);  // past nV: a copy, never used
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (tid + e * SEL_THREADS < a.nV) sbits[tid + e * SEL_THREADS] = v[e];
+    for (int e = 0; e < E; ++e) sbits[tid + e * SEL_THREADS] = v[e];
   }
   __syncthreads();
 
@@ -515,11 +518,10 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int x = lane + 64 * e;
-      v[e] = x < a.nV ? __float_as_uint(srow[x]) : 0u;
+      v[e] = __float_as_uint(srow[min(x, a.nV - 1)]);  // past nV: a copy, never used
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (lane + 64 * e < a.nV) sb[lane + 64 * e] = v[e];
+    for (int e = 0; e < E; ++e) sb[lane + 64 * e] = v[e];
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
