@@ -39,3 +39,39 @@ def select_rows(S: np.ndarray, N: int, block_k: int, k: int, m: int, seed: int, 
         idx[c::n_chunks] = ri
         w[c::n_chunks] = rw
     return idx, w
+
+
+def _seed_chunk(args):
+    S_rows, n_valid, k, m, seeds = args
+    idx = np.empty((len(seeds), len(S_rows), k + m), dtype=np.int32)
+    w = np.empty((len(seeds), len(S_rows), k + m), dtype=np.float32)
+    pis = None
+    for a, seed in enumerate(seeds):
+        for i, s in enumerate(S_rows):
+            ri, rw, info = oracle.select_row(s, n_valid, k, m, oracle.block_offset(seed, 0, 0, i), details=True)
+            idx[a, i], w[a, i] = ri, rw
+            if pis is None or len(pis) <= i:
+                pis = (pis or []) + [(info["R"], info["pi"])]
+    return idx, w, pis
+
+
+def select_seeds(S_rows: np.ndarray, N: int, block_k: int, k: int, m: int, seeds, workers: int = 8):
+    """oracle selection of query blocks i = 0.. of (b, h) = (0, 0) for every seed.
+
+    Returns (idx [seeds, rows, k+m], w [seeds, rows, k+m], [(R, pi_int) per row]).
+    """
+    S_rows = np.asarray(S_rows, dtype=np.float32)
+    n_valid = -(-N // block_k)
+    seeds = list(seeds)
+    workers = max(1, min(workers, len(os.sched_getaffinity(0))))
+    n_chunks = max(1, min(len(seeds), 4 * workers))
+    chunks = [seeds[c::n_chunks] for c in range(n_chunks)]
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(workers, mp_context=ctx) as ex:
+        outs = list(ex.map(_seed_chunk, [(S_rows, n_valid, k, m, ch) for ch in chunks]))
+    idx = np.empty((len(seeds), len(S_rows), k + m), dtype=np.int32)
+    w = np.empty((len(seeds), len(S_rows), k + m), dtype=np.float32)
+    for c, (ri, rw, _) in enumerate(outs):
+        idx[c::n_chunks] = ri
+        w[c::n_chunks] = rw
+    return idx, w, outs[0][2]

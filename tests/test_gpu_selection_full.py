@@ -9,7 +9,10 @@ the draw is word 0 of Philox4x32-10 at counter (i, h, b, 0) and key = seed).
 * 10,220 rows of the HunyuanVideo layer (every query block of 11 heads, 3,713
   valid 32-key units per row, the long-row kernel), S from bsa_score;
 * a sweep of 20 seeds over a 2-head 480p-shaped layer: 10,240 (counter, key)
-  pairs.
+  pairs;
+* 10,000 seeds on four 16-unit rows, every (seed, row) bit-exact, and the
+  empirical inclusion frequency of every unit against its pi (systematic
+  sampling takes unit j with probability pi_j whatever the offset's seed).
 The oracle's selection runs in CPU worker processes (tests/oracle_pool.py).
 """
 
@@ -20,7 +23,7 @@ import torch
 import block_sparse_attention_27_amd as bsa
 from block_sparse_attention_27_amd.inputs import WORKLOADS, generate
 from gpu_util import print_case, to_device
-from oracle_pool import select_rows
+from oracle_pool import select_rows, select_seeds
 
 pytestmark = pytest.mark.gpu
 
@@ -87,3 +90,43 @@ def test_selection_seed_sweep():
         idx, wt = bsa.select(ps, S)
         torch.cuda.synchronize()
         _compare(w, ps, S, idx, wt, rows, seed)
+
+
+def test_selection_ten_thousand_seeds_and_inclusion_frequencies():
+    """Four query blocks of 16 units (2 exact + 5 sampled): scores with a dominant
+    unit (capped at pi = 1), a zero, and a spread of gamma-distributed values."""
+    print_case("10,000 seeds x 4 rows of 16 units, k = 2, m = 5")
+    rng = np.random.default_rng(2024)
+    S_rows = rng.gamma(0.6, size=(4, 16)).astype(np.float32)
+    S_rows[0, 3] = 40.0   # dominant: capped
+    S_rows[1, 5] = 0.0    # quantised to the minimum
+    S_rows[2, :] = 1.0    # uniform row
+    S_rows /= S_rows.sum(axis=1, keepdims=True)
+    n_seeds = 10_000
+    p = bsa.Problem(B=1, H=1, N=512, N_pad=512, d=128, block_q=128, block_k=32, k_exact=2, m_sample=5,
+                    dtype=bsa.BSA_BF16, out_fp32=0, seed=0, sm_scale=1.0, kv_permuted=0)
+    S = torch.from_numpy(S_rows.reshape(1, 1, 4, 16)).cuda()
+    idx_all = torch.empty((n_seeds, 1, 1, 4, 7), dtype=torch.int32, device="cuda")
+    w_all = torch.empty((n_seeds, 1, 1, 4, 7), dtype=torch.float32, device="cuda")
+    for s in range(n_seeds):
+        p.seed = s * 0x9E3779B97F4A7C15 % (1 << 64)  # seeds spread over all 64 bits
+        bsa.bsa_select(p, S, idx_all[s], w_all[s])
+    torch.cuda.synchronize()
+    gi = idx_all.cpu().numpy().reshape(n_seeds, 4, 7)
+    gw = w_all.cpu().numpy().reshape(n_seeds, 4, 7)
+    seeds = [s * 0x9E3779B97F4A7C15 % (1 << 64) for s in range(n_seeds)]
+    ri, rw, pis = select_seeds(S_rows, 512, 32, 2, 5, seeds)
+    assert np.array_equal(gi, ri)
+    assert np.array_equal(gw.view(np.uint32), rw.view(np.uint32))
+    # empirical inclusion frequency of every unit of R in the sample part against pi
+    for i, (R, pi) in enumerate(pis):
+        counts = np.zeros(16)
+        for row in gi[:, i, 2:]:
+            counts[row] += 1
+        for pos, j in enumerate(R):
+            pj = pi[pos] / 2.0 ** 32
+            f = counts[j] / n_seeds
+            sigma = np.sqrt(pj * (1 - pj) / n_seeds)
+            assert abs(f - pj) <= 5 * sigma + 1e-12, (i, j, f, pj)
+        assert counts.sum() == 5 * n_seeds
+    print_case("  40,000 (seed, row) selections bit-exact; inclusion frequencies within 5 sigma of pi")
