@@ -204,7 +204,7 @@ def test_layer_score_select_attend(name):
     del out, lse, out16
 
 
-@pytest.mark.parametrize("name", ["wan13b", "hunyuan"])
+@pytest.mark.parametrize("name", ["wan13b", "wan14b_720p", "hunyuan"])
 def test_layer_dense(name):
     print_case(f"{name}: bsa_attend_dense vs oracle")
     w, g, dev = workload_data(name)
