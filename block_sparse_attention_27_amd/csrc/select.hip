@@ -86,19 +86,14 @@ __device__ __forceinline__ int frexp_exp(uint32_t x) {
   return (32 - __clz(mant)) - 149;
 }
 
-// floor(value(x) 2^(FS - e)), at least 1; exact integer arithmetic. Every x
-// is at most the maximum whose exponent is e, so value(x) < 2^e and the result
-// is below 2^FS: 32 bits hold it, and a left shift (x and the maximum both
-// subnormal) stays below 2^FS.
+// floor(value(x) 2^(FS - e)), at least 1. x is at most the maximum whose
+// exponent is e, so value(x) < 2^e and the scaled value is below 2^FS: scaling
+// by a power of two is exact unless the result underflows, and a result that
+// small is far below 1, whose floor (0) gives 1 either way. The conversion
+// truncates, which is the floor of a non-negative value.
 __device__ __forceinline__ uint32_t quantise(uint32_t x, int e) {
-  if (x == 0u) return 1u;
-  const int E = static_cast<int>(x >> 23);
-  const uint32_t sig = E ? ((x & 0x007FFFFFu) | 0x00800000u) : (x & 0x007FFFFFu);
-  const int shift = (E ? E : 1) - 150 + FS - e;
-  uint32_t q;
-  if (shift >= 0) q = sig << shift;
-  else q = shift > -32 ? sig >> (-shift) : 0u;
-  return q > 0u ? q : 1u;
+  const float v = __builtin_amdgcn_ldexpf(__uint_as_float(x), FS - e);
+  return max(1u, static_cast<uint32_t>(v));
 }
 
 // Cross-lane steps on DPP moves, which stay in the VALU (a lane shuffle is an
@@ -365,7 +360,10 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
 #pragma unroll
   for (int e = 0; e < E; ++e) q[e] = 0u;
   uint32_t thr = 0xFFFFFFFFu, delta = 0;
-  uint32_t pim1[E];  // pi - 1 on R (pi in [1, 2^32])
+  uint32_t pim1[E];  // pi - 1 on R (pi in [1, 2^32]), before the shortfall
+  // this thread's uncapped units, capped units and sum of pi over the uncapped ones
+  uint32_t nu = 0, ncap = 0;
+  uint64_t usum = 0;
   if (a.m > 0) {
     // ---- 2a. quantised scores over R ----
     uint32_t mx = 0;
@@ -413,15 +411,16 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
     // ratio fits 32 bits (>= 1).
     const uint32_t mt = static_cast<uint32_t>(a.m) - t;
     const double mt_d = static_cast<double>(mt), qu_d = static_cast<double>(QU);
-    uint64_t usum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       pim1[e] = 0xFFFFFFFFu;  // capped: pi = 2^32
+      ncap += q[e] >= thr ? 1u : 0u;
       if (q[e] != 0u && q[e] < thr) {
         const double ratio = (mt_d * static_cast<double>(q[e])) / qu_d;
         const uint32_t pv = static_cast<uint32_t>(ratio * 4294967296.0);
         pim1[e] = pv - 1u;
         usum += pv;
+        ++nu;
       }
     }
     // below the number of uncapped units: the floors lose less than 1 each
@@ -429,9 +428,6 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
   }
 
   // ---- ranks in unit order: K (high word) and uncapped R (low word) ----
-  uint32_t nu = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) nu += (q[e] != 0u && q[e] < thr) ? 1u : 0u;
   uint64_t rk_total;
   const uint64_t rk = block_exscan((static_cast<uint64_t>(__popc(fK)) << 32) | nu, red, par, rk_total);
   {  // the exact set, ascending, with w = 1
@@ -443,17 +439,13 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
   }
 
   if (a.m > 0) {
-    // the shortfall delta as +1 to the first delta uncapped units, then the
-    // sum of pi over this thread's units of R
-    uint32_t upos = static_cast<uint32_t>(rk);
-    uint64_t psum = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool unc = q[e] != 0u && q[e] < thr;
-      pim1[e] += (unc && upos < delta) ? 1u : 0u;
-      upos += unc ? 1u : 0u;
-      psum += q[e] != 0u ? static_cast<uint64_t>(pim1[e]) + 1u : 0u;
-    }
+    // The shortfall delta goes as +1 to the uncapped units of rank < delta; the
+    // uncapped units of this thread hold ranks u0 .. u0 + nu - 1. The sum of pi
+    // over its units of R follows without another pass: the uncapped pi, the
+    // shortfall it receives, and 2^32 for every capped unit.
+    const uint32_t u0 = static_cast<uint32_t>(rk);
+    const uint32_t n_short = min(nu, delta > u0 ? delta - u0 : 0u);
+    const uint64_t psum = usum + n_short + (static_cast<uint64_t>(ncap) << 32);
 
     // ---- 3. systematic sample over the cumulative pi axis: slot s sits at
     // u + s 2^32. This thread's units cover [c, c + psum); np is the first slot
@@ -468,13 +460,17 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
     // every key is in registers and the exscan's barrier has passed: the
     // staging array hands pi - 1 of each sampled slot (1 <= pi <= 2^32) to the
     // thread that writes its weight (k + m <= nV slots)
+    uint32_t upos = u0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      c += q[e] != 0u ? static_cast<uint64_t>(pim1[e]) + 1u : 0u;
+      const bool unc = q[e] != 0u && q[e] < thr;
+      const uint32_t pe = pim1[e] + ((unc && upos < delta) ? 1u : 0u);  // pi - 1 with the shortfall
+      upos += unc ? 1u : 0u;
+      c += q[e] != 0u ? static_cast<uint64_t>(pe) + 1u : 0u;
       if (c > np) {
         if (n < static_cast<uint32_t>(a.m)) {  // always, when sum pi = m 2^32
           irow[a.k + static_cast<int>(n)] = j0 + e;
-          sbits[n] = pim1[e];
+          sbits[n] = pe;
         }
         ++n;
         np += 1ull << 32;
@@ -616,7 +612,9 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
 #pragma unroll
   for (int e = 0; e < E; ++e) q[e] = 0u;
   uint32_t thr = 0xFFFFFFFFu, delta = 0;
-  uint32_t pim1[E];  // pi - 1 on R (pi in [1, 2^32])
+  uint32_t pim1[E];  // pi - 1 on R (pi in [1, 2^32]), before the shortfall
+  uint32_t nu = 0, ncap = 0;
+  uint64_t usum = 0;
   if (a.m > 0) {
     // ---- 2a. quantised scores over R ----
     uint32_t mx = 0;
@@ -653,24 +651,22 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
     // ---- 2c. fixed-point pi ----
     const uint32_t mt = static_cast<uint32_t>(a.m) - t;
     const double mt_d = static_cast<double>(mt), qu_d = static_cast<double>(QU);
-    uint64_t usum = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       pim1[e] = 0xFFFFFFFFu;  // capped: pi = 2^32
+      ncap += q[e] >= thr ? 1u : 0u;
       if (q[e] != 0u && q[e] < thr) {
         const double ratio = (mt_d * static_cast<double>(q[e])) / qu_d;
         const uint32_t pv = static_cast<uint32_t>(ratio * 4294967296.0);
         pim1[e] = pv - 1u;
         usum += pv;
+        ++nu;
       }
     }
     delta = static_cast<uint32_t>((static_cast<uint64_t>(mt) << 32) - wave_sum(usum));
   }
 
   // ---- ranks in unit order: K (high word) and uncapped R (low word) ----
-  uint32_t nu = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) nu += (q[e] != 0u && q[e] < thr) ? 1u : 0u;
   uint64_t rk_total;
   const uint64_t rk = wave_exscan((static_cast<uint64_t>(__popc(fK)) << 32) | nu, rk_total);
   {
@@ -682,15 +678,10 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
   }
 
   if (a.m > 0) {
-    uint32_t upos = static_cast<uint32_t>(rk);
-    uint64_t psum = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool unc = q[e] != 0u && q[e] < thr;
-      pim1[e] += (unc && upos < delta) ? 1u : 0u;
-      upos += unc ? 1u : 0u;
-      psum += q[e] != 0u ? static_cast<uint64_t>(pim1[e]) + 1u : 0u;
-    }
+    // the sum of pi over this lane's units of R without another pass, as in select_kernel
+    const uint32_t u0 = static_cast<uint32_t>(rk);
+    const uint32_t n_short = min(nu, delta > u0 ? delta - u0 : 0u);
+    const uint64_t psum = usum + n_short + (static_cast<uint64_t>(ncap) << 32);
 
     // ---- 3. systematic sample over the cumulative pi axis ----
     uint64_t ptotal;
@@ -704,13 +695,17 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t upos = u0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      c += q[e] != 0u ? static_cast<uint64_t>(pim1[e]) + 1u : 0u;
+      const bool unc = q[e] != 0u && q[e] < thr;
+      const uint32_t pe = pim1[e] + ((unc && upos < delta) ? 1u : 0u);  // pi - 1 with the shortfall
+      upos += unc ? 1u : 0u;
+      c += q[e] != 0u ? static_cast<uint64_t>(pe) + 1u : 0u;
       if (c > np) {
         if (n < static_cast<uint32_t>(a.m)) {  // k + m <= nV <= 64 E slots
           irow[a.k + static_cast<int>(n)] = j0 + e;
-          sb[n] = pim1[e];
+          sb[n] = pe;
         }
         ++n;
         np += 1ull << 32;
