@@ -211,6 +211,17 @@ __device__ __forceinline__ uint64_t block_exscan(uint64_t v, BlockRed& r, int& p
   return before + x - v;
 }
 
+// Every key lies between the smallest and the largest, so all of them (and
+// the k-th largest) share the bits above the highest bit where those two
+// differ: the bitwise search starts below it, from that common prefix.
+// Returns the highest differing bit (-1 when every key is equal) and sets T.
+__device__ __forceinline__ int common_prefix(uint32_t kmin, uint32_t kmax, uint32_t& T) {
+  const uint32_t diff = kmin ^ kmax;
+  const int top = diff ? 31 - __clz(diff) : -1;
+  T = top >= 0 ? kmax & ~((2u << top) - 1u) : kmax;  // top = 31 cannot occur: keys are below 2^31
+  return top;
+}
+
 // ceil(x / d) for d >= 1: the smallest q with d q >= x.
 __device__ __forceinline__ uint32_t level(uint32_t x, uint32_t d) { return x / d + (x % d != 0u ? 1u : 0u); }
 
@@ -271,7 +282,30 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
     // barrier per bit: a buffer is rewritten two bits later, after every
     // thread has passed the barrier that follows its reads
     const int wave = tid / 64, lane = tid % 64;
-    uint32_t T = 0;
+    uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      kmax = max(kmax, valid(e) ? key[e] : 0u);
+      kmin = min(kmin, valid(e) ? key[e] : 0xFFFFFFFFu);
+    }
+    {  // both extremes in one reduction: the maximum of the keys and of their complements
+      kmax = wave_max_u32(kmax);
+      kmin = ~wave_max_u32(~kmin);
+      uint64_t* rr = red.r64[par];
+      par ^= 1;
+      if (lane == 0) rr[wave] = (static_cast<uint64_t>(kmax) << 32) | ~kmin;
+      __syncthreads();
+      uint32_t m0 = 0, m1 = 0;
+#pragma unroll
+      for (int x = 0; x < SEL_WAVES; ++x) {
+        m0 = max(m0, static_cast<uint32_t>(rr[x] >> 32));
+        m1 = max(m1, static_cast<uint32_t>(rr[x]));
+      }
+      kmax = m0;
+      kmin = ~m1;
+    }
+    uint32_t T;
+    const int top_bit = common_prefix(kmin, kmax, T);
     auto block_bits = [&](int top, int low) {
       for (int bit = top; bit >= low; --bit) {
         const uint32_t cand = T | (1u << bit);
@@ -286,7 +320,7 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
         if (tot >= static_cast<uint32_t>(a.k)) T = cand;
       }
     };
-    block_bits(30, SPLIT);
+    block_bits(top_bit, SPLIT);
     // keys above T's bin, and the keys in it (hi may be 2^31: no key reaches it)
     const uint32_t hi = T + (1u << SPLIT);
     uint32_t n_above = 0, n_play = 0;
@@ -314,7 +348,7 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
           const uint32_t x = static_cast<uint32_t>(lane + 64 * z);
           ck[z] = x < play ? sbits[x] : 0u;  // padding 0 never reaches cand >= 1
         }
-        for (int bit = SPLIT - 1; bit >= 0; --bit) {
+        for (int bit = min(SPLIT - 1, top_bit); bit >= 0; --bit) {
           const uint32_t cand = T | (1u << bit);
           uint32_t c = 0;
 #pragma unroll
@@ -326,7 +360,7 @@ __global__ __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(6))
       __syncthreads();
       T = t_bcast;
     } else {
-      block_bits(SPLIT - 1, 0);
+      block_bits(min(SPLIT - 1, top_bit), 0);
     }
     uint32_t gt = 0, eq = 0;
 #pragma unroll
@@ -539,8 +573,15 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
   // ---- 1. exact set: the top bits over every key, the low bits over the
   // keys in the threshold's bin (compacted into the wave's slice) ----
   if (a.k > 0) {
-    uint32_t T = 0;
-    for (int bit = 30; bit >= SPLIT; --bit) {
+    uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      kmax = max(kmax, valid(e) ? key[e] : 0u);
+      kmin = min(kmin, valid(e) ? key[e] : 0xFFFFFFFFu);
+    }
+    uint32_t T;
+    const int top_bit = common_prefix(~wave_max_u32(~kmin), wave_max_u32(kmax), T);
+    for (int bit = top_bit; bit >= SPLIT; --bit) {
       const uint32_t cand = T | (1u << bit);
       uint32_t c = 0;  // cand >= 1, and invalid units hold key 0
 #pragma unroll
@@ -576,7 +617,7 @@ __global__ __launch_bounds__(64 * SELW_WAVES) void select_wave_kernel(SelectArgs
         const uint32_t x = static_cast<uint32_t>(lane + 64 * z);
         ck[z] = (z < chunks && x < play) ? sb[x] : 0u;  // padding 0 never reaches cand >= 1
       }
-      for (int bit = SPLIT - 1; bit >= 0; --bit) {
+      for (int bit = min(SPLIT - 1, top_bit); bit >= 0; --bit) {
         const uint32_t cand = T | (1u << bit);
         uint32_t c = 0;
 #pragma unroll
