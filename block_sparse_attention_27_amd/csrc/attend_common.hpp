@@ -246,10 +246,19 @@ __device__ __forceinline__ void stage_gathered(const uint16_t* src, BSA_LDS char
 // Rank-sorts the list chunk [c0, c0 + n) of one query block by unit index
 // (ties by position) into the LDS tables; entries with an index outside
 // [0, nKU) or a weight that is not a finite positive number become empty.
+// The rank of entry e is the number of keys below its own plus the equal keys
+// before it. A list made of a few ascending runs (a bsa_select list is two:
+// the exact set, then the sample in unit order) gets it from binary searches
+// of the other runs; any other list from a scan of the whole chunk.
+constexpr int SORT_MAX_RUNS = 4;
+
 template <int NT, int BK>
 __device__ __forceinline__ void sort_list(const AttendArgs& a, const int32_t* idx_row, const float* w_row,
                                           int c0, int n, int* s_key, int* s_base, int* s_lim, float* s_lw,
                                           int tid) {
+  __shared__ int s_nruns;                     // descents found (runs - 1)
+  __shared__ int s_start[SORT_MAX_RUNS - 1];  // positions that start a run after the first, unordered
+  if (tid == 0) s_nruns = 0;
   for (int e = tid; e < n; e += NT) {
     const int j = idx_row[c0 + e];
     const float wv = w_row[c0 + e];
@@ -257,12 +266,58 @@ __device__ __forceinline__ void sort_list(const AttendArgs& a, const int32_t* id
     s_key[e] = ok ? j : 0x7FFFFFFF;
   }
   __syncthreads();
+  for (int e = 1 + tid; e < n; e += NT) {
+    if (s_key[e - 1] > s_key[e]) {
+      const int slot = atomicAdd(&s_nruns, 1);
+      if (slot < SORT_MAX_RUNS - 1) s_start[slot] = e;
+    }
+  }
+  __syncthreads();
+  const int nd = s_nruns;  // uniform
+  int start[SORT_MAX_RUNS + 1];  // run r is [start[r], start[r + 1]), ascending
+  const bool runs = nd < SORT_MAX_RUNS;
+  if (runs) {
+    start[0] = 0;
+#pragma unroll
+    for (int r = 1; r < SORT_MAX_RUNS; ++r) start[r] = r <= nd ? s_start[r - 1] : n;
+#pragma unroll
+    for (int r = 1; r < SORT_MAX_RUNS; ++r)  // insertion sort of the (at most three) starts
+#pragma unroll
+      for (int q = r; q > 1; --q)
+        if (start[q - 1] > start[q]) {
+          const int t = start[q - 1];
+          start[q - 1] = start[q];
+          start[q] = t;
+        }
+    start[SORT_MAX_RUNS] = n;
+  }
   for (int e = tid; e < n; e += NT) {
     const int my = s_key[e];
     int rank = 0;
-    for (int e2 = 0; e2 < n; ++e2) {
-      const int k2 = s_key[e2];
-      rank += (k2 < my || (k2 == my && e2 < e)) ? 1 : 0;
+    if (runs) {
+#pragma unroll
+      for (int r = 0; r < SORT_MAX_RUNS; ++r) {
+        const int lo = start[r], hi = start[r + 1];
+        if (e >= lo && e < hi) {
+          rank += e - lo;  // the run's entries before e are all <= my
+        } else {
+          // entries of run r below my (equal ones too when the run comes first)
+          const bool before = hi <= e;
+          int l = lo, h = hi;
+          while (l < h) {
+            const int mid = (l + h) >> 1;
+            const int k2 = s_key[mid];
+            if (k2 < my || (before && k2 == my)) l = mid + 1;
+            else h = mid;
+          }
+          rank += l - lo;
+        }
+      }
+    } else {
+      for (int e2 = 0; e2 < n; ++e2) {
+        const int k2 = s_key[e2];
+        rank += (k2 < my || (k2 == my && e2 < e)) ? 1 : 0;
+      }
     }
     const bool ok = my != 0x7FFFFFFF;
     const int b0 = ok ? my * BK : 0;

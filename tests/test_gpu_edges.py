@@ -146,6 +146,38 @@ def test_ignored_and_repeated_list_entries():
     assert rel_l2(got, ref) <= 2e-3 and np.max(np.abs(got - ref)) <= 1e-2
 
 
+@pytest.mark.parametrize("bq", [64, 128])
+@pytest.mark.parametrize("runs", [1, 2, 3, 4, 5, 12])
+def test_list_made_of_ascending_runs(bq, runs):
+    """The kernels rank a list of a few ascending runs by binary searches and any
+    other list by a full scan; both must give the oracle's result, with units
+    repeated inside and across runs (ties keep their list order)."""
+    print_case(f"lists of {runs} ascending runs, bq={bq}")
+    w = _small(128, bq, 32, "bf16", False, k=10, m=20)
+    g = generate(w)
+    q, k, v = (to_device(g[x]) for x in ("q", "k", "v"))
+    p = bsa.problem_for(w, out_fp32=1)
+    rng = np.random.default_rng(100 + runs)
+    shape = (w.B, w.H, w.n_qblocks, w.list_len)
+    idx = rng.integers(0, w.n_valid_units, shape).astype(np.int32)
+    cuts = np.sort(rng.choice(np.arange(1, w.list_len), runs - 1, replace=False)) if runs > 1 else []
+    for seg in np.split(np.arange(w.list_len), cuts):
+        idx[..., seg] = np.sort(idx[..., seg], axis=-1)
+    wts = (0.5 + 3.5 * rng.random(shape)).astype(np.float32)
+    out = bsa.attend(p, q, k, v, torch.from_numpy(idx).cuda(), torch.from_numpy(wts).cuda())
+    torch.cuda.synchronize()
+    qh, kh, vh = (host_f64(g[x]) for x in ("q", "k", "v"))
+    got = to_f64(out)
+    ref = np.zeros_like(got)
+    for b in range(w.B):
+        for h in range(w.H):
+            for i in range(w.n_qblocks):
+                rows = slice(i * w.block_q, (i + 1) * w.block_q)
+                ref[b, h, rows], _ = oracle.attend_block(qh[b, h], kh[b, h], vh[b, h], i, idx[b, h, i], wts[b, h, i],
+                                                         w.N, w.block_q, w.block_k, w.sm_scale)
+    assert rel_l2(got, ref) <= 2e-3 and np.max(np.abs(got - ref)) <= 1e-2
+
+
 def _hostile_rows(n_rows, n_valid, n_units, rng):
     S = np.zeros((n_rows, n_units), dtype=np.float32)
     for r in range(n_rows):
