@@ -70,7 +70,7 @@ __device__ __forceinline__ TileMeta tile_meta64(const AttendArgs& a, const int* 
   return m;
 }
 
-// Instruction i of a tile's staging, without branches (no permutation): the
+// Instruction i of a tile's staging, without branches (K and V read in place): the
 // lane's row is i G + r0 of the tile; rows past a slot's valid keys load the
 // slot's last valid key (an empty slot, base 0 and no keys: row 0), so the
 // address is the slot's first row (uniform) plus min(row in slot, last valid
@@ -91,7 +91,7 @@ __device__ __forceinline__ void stage64_ins(const uint16_t* src, BSA_LDS char* d
                                    (BSA_LDS void*)(dst + (i * NW64 + swave) * 1024), 16, 0, 0);
 }
 
-// Gathered key row of tile row r for a permuted sequence: slot r / S, key
+// Gathered key row of tile row r when K and V go through perm: slot r / S, key
 // r % S -> perm[base + r % S]; a row past the slot's valid keys, or a gather
 // entry outside [0, N_pad), gives row 0 of the head (its logits are masked).
 template <int S>
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
   __shared__ int s_base[DENSE ? 1 : LMAX64];
   __shared__ int s_lim[DENSE ? 1 : LMAX64];
   __shared__ float s_lw[DENSE ? 1 : LMAX64];
-  // permuted sequences: gathered key rows of tiles t+1 .. t+3, slot (t & 3)
+  // K and V through perm: gathered key rows of tiles t+1 .. t+3, slot (t & 3)
   __shared__ int s_grow[PERM ? 4 * T64 : 1];
   static_assert(LMAX64 * 4 <= TB, "the sort keys borrow a tile slot");
 
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(64 * NW64, 2) void attend_t64_kernel(AttendArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) kf[i] = kread(i);
       const TileMeta mt2 = meta_of(t + 2);
-      // Staging of K(t+2) and V(t+1). With a permutation all of it happens
+      // Staging of K(t+2) and V(t+1). With K and V gathered all of it happens
       // here, from the gathered rows the step before last looked up, and this
       // step looks up tile t+3's rows (stored at its end); otherwise one load
       // per few MFMA groups below, branch-free: past the end of the list the

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
   __shared__ int s_base[DENSE ? 1 : LMAX];
   __shared__ int s_lim[DENSE ? 1 : LMAX];
   __shared__ float s_lw[DENSE ? 1 : LMAX];
-  // permuted sequences: gathered key rows of tiles t+1 .. t+3, slot (t & 3)
+  // K and V through perm: gathered key rows of tiles t+1 .. t+3, slot (t & 3)
   __shared__ int s_grow[PERM ? 4 * TILE : 1];
 
   const int tid = threadIdx.x;
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void attend_w32_kernel(AttendArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) kf[i] = kread(i);
       const TileMeta mt2 = meta_of(t + 2);
-      // Staging of K(t+2) and V(t+1). With a permutation all of it happens
+      // Staging of K(t+2) and V(t+1). With K and V gathered all of it happens
       // here, from the gathered rows the step before last looked up, and this
       // step looks up tile t+3's rows (stored at its end); otherwise one load
       // per few MFMA groups below, branch-free: past the end of the list the

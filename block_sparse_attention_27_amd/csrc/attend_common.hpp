@@ -107,7 +107,7 @@ __device__ __forceinline__ int gather_row(const AttendArgs& a, int r, bool& ok) 
 }
 
 struct TileMeta {
-  int base[4];  // first global (pre-permutation) key row of each unit in the tile
+  int base[4];  // first key row of each unit in the tile, in the order K and V are given
   int lim[4];   // valid keys of each unit (0: empty slot or rejected entry)
   float lw[4];  // log2 of the unit's weight
   bool full;    // every unit of the tile holds BK valid keys
@@ -159,8 +159,8 @@ __device__ __forceinline__ void stage_fast(const uint16_t* src, BSA_LDS char* ds
                                    (BSA_LDS void*)(dst + (i * NW + swave) * 1024), 16, 0, 0);
 }
 
-// The whole tile on the general path: partial or empty units, or a
-// permutation. Rows past a unit's valid keys load a valid row of the same
+// The whole tile on the general path: partial or empty units, or K and V
+// gathered through perm. Rows past a unit's valid keys load a valid row of the same
 // head instead (their logits are masked).
 template <int D, int NW, int BK, bool PERM, bool IS_V>
 __device__ __forceinline__ void stage_general(const AttendArgs& a, const uint16_t* src, BSA_LDS char* dst,
@@ -199,7 +199,7 @@ __device__ __forceinline__ void stage_one(const AttendArgs& a, const uint16_t* s
   }
 }
 
-// Instruction i of a tile's staging, without branches (no permutation):
+// Instruction i of a tile's staging, without branches (K and V read in place):
 // rows past a unit's valid keys load the unit's last valid key (an empty
 // slot, base 0 and no keys: row 0), so the address is the unit's first row
 // (uniform) plus min(row in unit, last valid row) 2D + the lane's chunk byte.
@@ -219,7 +219,7 @@ __device__ __forceinline__ void stage_ins(const uint16_t* src, BSA_LDS char* dst
                                    (BSA_LDS void*)(dst + (i * NW + swave) * 1024), 16, 0, 0);
 }
 
-// Gathered key row of tile row r for a permuted sequence: unit r / BK, key
+// Gathered key row of tile row r when K and V go through perm: unit r / BK, key
 // r % BK -> perm[base + r % BK]; a row past the unit's valid keys, or a gather
 // entry outside [0, N_pad), gives row 0 of the head (its logits are masked).
 template <int BK>
@@ -230,7 +230,7 @@ __device__ __forceinline__ int tile_row_gather(const AttendArgs& a, const TileMe
   return static_cast<unsigned>(g) < static_cast<unsigned>(a.N_pad) ? g : 0;
 }
 
-// Instruction i of a tile's staging for a permuted sequence: the tile's
+// Instruction i of a tile's staging with K and V gathered through perm: the tile's
 // gathered rows come from an LDS table (rows[r] for tile row r), so the
 // address is the lane's gathered row plus its fixed chunk byte.
 template <int D, int NW>

@@ -20,17 +20,18 @@
 //   4. emit K ascending with w = 1, then sample slot s -> its unit with
 //      w = fp32(2^32 / pi_int).
 // Every sum is an integer sum, so the result is independent of reduction
-// order and bit-identical to the CPU definition. The only floating-point
-// operations are two correctly rounded fp64 divisions and one fp64 -> fp32
-// rounding.
+// order and bit-identical to the CPU definition. Besides exact power-of-two
+// scalings and conversions, the only floating-point operations are two
+// correctly rounded fp64 divisions and one fp64 -> fp32 rounding.
 //
 // Layout: thread t owns the E consecutive units [t E, t E + E), so exclusive
 // scans give ranks in unit order directly. Rows of up to 1024 valid units take
 // one wave each (ballot counts, DPP sums and scans, no barriers); longer rows take a
 // 256-thread workgroup. The threshold of the exact set is found bit by bit,
-// most significant first: the top 12 bits over every key, the low 19 over the
-// few keys that share the threshold's top bits, gathered into LDS (one wave
-// finishes them without barriers).
+// most significant first, below the bits that every key shares: the top 12
+// bits over every key, the low 19 over the few keys that share the
+// threshold's top bits, gathered into LDS (one wave finishes them without
+// barriers).
 #include "bsa_internal.hpp"
 
 namespace bsa {
