@@ -202,9 +202,13 @@ bsa_status bsa_select(const bsa_problem* p, const float* S, int32_t* idx, float*
  * (InstaGen, Abstract: permuted block-sparse attention computes blocks of an
  * attention matrix whose tokens have been reordered by semantic similarity.)
  * Puts K and V into the permuted order once, for calls with kv_permuted = 1.
- * x and x_perm are [B][H][N_pad][d] of `dtype`, 16-byte aligned, and must not
- * overlap; perm is required. Uses B, H, N, N_pad, d and dtype of p. A pure
- * copy of bytes: bit-exact.
+ * x and x_perm are [B][H][N_pad][d] of `dtype`, 16-byte aligned device
+ * buffers owned by the caller, and must not overlap; perm is required. Uses B,
+ * H, N, N_pad, d and dtype of p (the other fields are checked as in every
+ * call but not used). A pure copy of bytes: bit-exact. Errors: a null or
+ * misaligned pointer, a missing perm or overlapping buffers give
+ * BSA_ERR_INVALID_ARG; more than 2^31 - 1024 16-byte chunks per (b, h), or a
+ * grid beyond 2^32 work-items, give BSA_ERR_UNSUPPORTED.
  */
 bsa_status bsa_permute_rows(const bsa_problem* p, const void* x, const int32_t* perm, void* x_perm,
                             hipStream_t stream);
