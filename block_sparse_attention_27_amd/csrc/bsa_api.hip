@@ -67,6 +67,10 @@ bool perm_ok(const bsa::Geometry& g, const int32_t* perm) {
 
 bsa_status from_hip(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
 
+// The scoring kernels read one head's key means through a buffer resource
+// whose byte count (nKU * d * 4) is a 32-bit record count.
+bool score_units_ok(const bsa::Geometry& g) { return static_cast<int64_t>(g.nKU) * g.d * 4 <= 0x7FFFFFFFll; }
+
 }  // namespace
 
 namespace bsa {
@@ -103,6 +107,7 @@ bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const i
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(S, 4) || !aligned(q_mean, 16) || !aligned(k_mean, 16))
     return BSA_ERR_INVALID_ARG;
   if (!perm_ok(g, perm)) return BSA_ERR_INVALID_ARG;
+  if (!score_units_ok(g)) return BSA_ERR_UNSUPPORTED;
   st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, nullptr, false, stream));
   if (st != BSA_OK) return st;
   return from_hip(bsa::launch_scores(g, 1, q_mean, nullptr, k_mean, nullptr, S, stream));
@@ -118,6 +123,7 @@ bsa_status bsa_score_stats(const bsa_problem* p, const void* q, const void* k, c
       !aligned(k_var, 16))
     return BSA_ERR_INVALID_ARG;
   if (!perm_ok(g, perm)) return BSA_ERR_INVALID_ARG;
+  if (!score_units_ok(g)) return BSA_ERR_UNSUPPORTED;
   st = from_hip(bsa::launch_block_means(g, q, k, perm, q_mean, k_mean, k_var, false, stream));
   if (st != BSA_OK) return st;
   return from_hip(bsa::launch_scores(g, 1, q_mean, nullptr, k_mean, k_var, S, stream));
@@ -136,6 +142,7 @@ bsa_status bsa_score_ibcs(const bsa_problem* p, int32_t groups, int32_t iters, c
       !aligned(k_mean, 16))
     return BSA_ERR_INVALID_ARG;
   if (!perm_ok(g, perm)) return BSA_ERR_INVALID_ARG;
+  if (!score_units_ok(g)) return BSA_ERR_UNSUPPORTED;
   st = from_hip(bsa::launch_block_means(g, q, k, perm, nullptr, k_mean, nullptr, true, stream));
   if (st != BSA_OK) return st;
   st = from_hip(bsa::launch_block_clusters(g, groups, iters, q, perm, q_cent, q_size, stream));

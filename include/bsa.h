@@ -110,7 +110,10 @@ const char* bsa_status_string(int32_t status);
  *       l_ij = sm_scale <q_mean_i, k_mean_j>;  S = 0 for invalid units.
  * A query block with no valid row has q_mean = 0. Uses q, k (dtype), perm
  * (optional, see above). q_mean is [B][H][nQB][d], k_mean [B][H][nKU][d];
- * both are written (the caller owns them; 16-byte aligned).
+ * both are written (the caller owns them; 16-byte aligned). One head's key
+ * means are read as one 32-bit-addressed range: nKU * d * 4 above 2^31 - 1
+ * bytes (more than 4,194,303 key units at d = 128) gives BSA_ERR_UNSUPPORTED,
+ * here and in bsa_score_stats and bsa_score_ibcs.
  */
 bsa_status bsa_score(const bsa_problem* p, const void* q, const void* k, const int32_t* perm,
                      float* S, float* q_mean, float* k_mean, hipStream_t stream);

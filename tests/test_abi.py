@@ -183,6 +183,16 @@ def test_selection_unit_limit_is_unsupported(lib):
     assert lib.bsa_select(p, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_UNSUPPORTED
 
 
+def test_scoring_key_unit_limit_is_unsupported(lib):
+    # 2^22 units of 32 keys at d = 128: one head's key means span 2^31 bytes,
+    # one more than the kernels' 32-bit range; at d = 64 the same shape passes
+    # this check (and would launch, so it is not called here)
+    p = ctypes.byref(_good(N=1 << 27, N_pad=1 << 27, block_k=32, block_q=128, H=1))
+    assert lib.bsa_score(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_UNSUPPORTED
+    assert lib.bsa_score_ibcs(p, 4, 3, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_UNSUPPORTED
+    assert lib.bsa_score_stats(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setenv("BSA_LIBRARY", str(tmp_path / "missing.so"))
     monkeypatch.setattr(bsa, "_lib", None)
