@@ -17,7 +17,11 @@ values. On the whole tensors, in the launch configuration of the full layers:
   bit-exact) and bsa_attend on 32-key units with lists of 12 units, once with
   K and V permuted first (kv_permuted = 1) and once gathering inside: the two
   outputs are bit-identical over the whole tensor and match the oracle on
-  sampled blocks.
+  sampled blocks;
+* bsa_attend on 64-row query blocks and 64-key units, K and V gathered through
+  the index inside (the 8-wave kernel);
+* fp32 Q, K and V (9.1 GB each): scores, selection and the fp32 attention
+  kernel, within 1e-5 of the oracle.
 
 Bars as in the full-layer parity tests: scores 1e-3 relative, selection
 bit-exact, attention 2e-3 relative L2 and 1e-2 max-abs, lse 2e-3.
@@ -178,13 +182,7 @@ def test_permuted_32_key_units_past_2e31_elements(data):
             want = np.where((r < W.N)[:, None], src[0, j, np.where(r < W.N, perm[r], 0)], 0)
             assert np.array_equal(rows, want), (name, h)
 
-    # lists of 12 distinct 32-key units per query block, in no particular order, weights in [0.5, 4)
-    L = 12
-    shape = (W.B, W.H, W.n_qblocks, L)
-    start = rng.integers(0, n_valid, (W.B, W.H, W.n_qblocks, 1))
-    idx = ((start + 1361 * np.arange(L)) % n_valid).astype(np.int32)  # 12 x 1361 < n_valid: distinct
-    idx = np.take_along_axis(idx, np.argsort(rng.random(shape), axis=-1), axis=-1)
-    wt = rng.uniform(0.5, 4.0, shape).astype(np.float32)
+    idx, wt = _explicit_lists(rng, (W.B, W.H, W.n_qblocks), n_valid, 12, 1361)
     idx_d, wt_d = torch.from_numpy(idx).cuda(), torch.from_numpy(wt).cuda()
 
     print_case(f"{W.name}: bsa_attend on 32-key units, K and V permuted first and gathered inside")
@@ -208,3 +206,78 @@ def test_permuted_32_key_units_past_2e31_elements(data):
         got_rows += gr
         ref_rows += rr
     _check_rows(got_rows, ref_rows, "permuted sparse attention")
+
+
+def _explicit_lists(rng, n_rows_shape, n_valid, L, step):
+    """L distinct valid units per row (start + step e mod n_valid, L step < n_valid), shuffled; weights in [0.5, 4)."""
+    assert L * step < n_valid
+    shape = n_rows_shape + (L,)
+    start = rng.integers(0, n_valid, n_rows_shape + (1,))
+    idx = ((start + step * np.arange(L)) % n_valid).astype(np.int32)
+    idx = np.take_along_axis(idx, np.argsort(rng.random(shape), axis=-1), axis=-1)
+    wt = rng.uniform(0.5, 4.0, shape).astype(np.float32)
+    return idx, wt
+
+
+def test_64_row_blocks_gathered_past_2e31_elements(data):
+    g, dev = data
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    perm = g["perm"]
+    bq = bk = 64
+    p = bsa.problem_for(W, block_q=bq, block_k=bk, k_exact=4, m_sample=4, out_fp32=1)
+    nQB = W.N_pad // bq
+    n_valid = -(-W.N // bk)
+    idx, wt = _explicit_lists(np.random.default_rng(5), (W.B, W.H, nQB), n_valid, 8, 1013)
+    print_case(f"{W.name}: bsa_attend on 64-row query blocks, K and V gathered through perm inside")
+    out, lse = bsa.attend(p, q, k, v, torch.from_numpy(idx).cuda(), torch.from_numpy(wt).cuda(),
+                          torch.from_numpy(perm).cuda(), with_lse=True)
+    torch.cuda.synchronize()
+    blocks = [0, nQB // 2, nQB - 1]
+    got_rows, ref_rows = [], []
+    for h in (0, 33):
+        qh, kh, vh = (_host_head(g, x, h) for x in ("q", "k", "v"))
+        refs = oracle.attend(qh, kh, vh, W.N, bq, bk, W.sm_scale, idx[:, h:h + 1], wt[:, h:h + 1], perm,
+                             blocks=[(0, 0, i) for i in blocks])
+        gr, rr = _check_blocks(out, lse, refs, h, blocks, bq, perm)
+        got_rows += gr
+        ref_rows += rr
+    _check_rows(got_rows, ref_rows, "64-row blocks")
+
+
+def test_fp32_inputs_past_2e31_elements(data):
+    """fp32 Q, K, V (9.1 GB each): block means, scores, selection and the fp32 attention kernel."""
+    g, dev = data
+    q, k, v = (dev[x].float() for x in ("q", "k", "v"))  # exact widening of the bf16 values
+    p = bsa.problem_for(W, dtype=bsa.BSA_FP32)
+    print_case(f"{W.name}: fp32 inputs, bsa_score, bsa_select, bsa_attend over {W.H} heads")
+    S, _, _ = bsa.score(p, q, k)
+    idx, wt = bsa.select(p, S)
+    out, lse = bsa.attend(p, q, k, v, idx, wt, with_lse=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    nQB = W.n_qblocks
+    blocks = [0, nQB // 2, nQB - 1]
+    S_rows = np.zeros(S.shape, dtype=np.float32)
+    rows = []
+    for h in (0, 33):
+        qh, kh, vh = (_host_head(g, x, h) for x in ("q", "k", "v"))
+        S_ref, _, _ = oracle.score(qh, kh, W.N, W.block_q, W.block_k, W.sm_scale)
+        got = S[0, h].cpu().numpy().astype(np.float64)
+        ref = S_ref[0, 0].astype(np.float64)
+        bad = np.abs(got - ref) > SCORE_RTOL * ref + 1e-12 * ref.max(axis=-1, keepdims=True)
+        assert not bad.any(), (h, int(bad.sum()))
+        S_rows[0, h] = S[0, h].cpu().numpy()
+        rows += [(0, h, i) for i in blocks]
+        refs = oracle.attend(qh, kh, vh, W.N, W.block_q, W.block_k, W.sm_scale, idx[0:1, h:h + 1].cpu().numpy(),
+                             wt[0:1, h:h + 1].cpu().numpy(), blocks=[(0, 0, i) for i in blocks])
+        gr, rr = _check_blocks(out, lse, refs, h, blocks, W.block_q)
+        got = np.concatenate(gr)
+        ref = np.concatenate(rr)
+        r, m = rel_l2(got, ref), float(np.max(np.abs(got - ref)))
+        print_case(f"  head {h}: fp32 attention rel_l2={r:.3e} max_abs={m:.3e}")
+        assert r < 1e-5 and m < 1e-5, (h, r, m)
+    idx_all, wt_all = idx.cpu().numpy(), wt.cpu().numpy()
+    for (b, h, i), (ri, rw) in zip(rows, oracle.select(S_rows, W.N, W.block_k, W.k_exact, W.m_sample,
+                                                        W.select_seed, rows=rows)):
+        assert np.array_equal(idx_all[b, h, i], ri), (b, h, i)
+        assert np.array_equal(wt_all[b, h, i].view(np.uint32), rw.view(np.uint32)), (b, h, i)
