@@ -15,7 +15,9 @@ score + select followed by r attend calls that reuse its lists; `ibcs` times
 the intra-block clustering scorer in place of bsa_score, `stats` the
 statistics-aware scorer.
 `roofline` describes bsa_attend (bf16 MFMA bound), timed with HIP events on
-the stream it runs on; `cpu_baseline` is the fp64 CPU oracle timed on a
+the stream it runs on; `mfma_ceiling` is the rate a register-only MFMA loop
+sustains on the same chip (its clock falls under a long matrix load), and
+`attend_frac_of_ceiling` bsa_attend's rate against it; `cpu_baseline` is the fp64 CPU oracle timed on a
 bounded sample of the same workload on this host's cores.
 """
 
@@ -113,6 +115,31 @@ def cpu_baseline(w, g, budget_s: float = 20.0):
                         "attend_per_block": round(t_attend_block, 5)}}
 
 
+def mfma_ceiling(bsa, torch, iters: int = 40000, n_wg: int = 512, reps: int = 5) -> dict:
+    """Sustained bf16 MFMA rate of this chip: bsa_mfma_ceiling, 2 workgroups per CU, ~10 ms per launch.
+
+    Under a long matrix load the clock drops to hold the power limit, so this
+    register-only loop is the ceiling any matrix-bound kernel meets here.
+    """
+    stream = torch.cuda.current_stream()
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        bsa.bsa_mfma_ceiling(out, iters, n_wg)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        bsa.bsa_mfma_ceiling(out, iters, n_wg)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+    flop = n_wg * 4 * iters * bsa.MFMA_CEILING_FLOP
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "ms_per_launch": round(ms, 3),
+            "kernel": f"bsa_mfma_ceiling: {n_wg} workgroups of 4 waves, {iters} rounds of 8 register-only "
+                      "v_mfma_f32_32x32x16_bf16 per wave"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +150,9 @@ def main(argv=None):
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the sustained-MFMA-rate measurement")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="only measure the sustained MFMA rate (bsa_mfma_ceiling) and print it")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -136,6 +166,10 @@ def main(argv=None):
 
     import block_sparse_attention_27_amd as bsa
     from block_sparse_attention_27_amd.inputs import WORKLOADS, generate
+
+    if args.ceiling_only:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(bsa, torch)}), flush=True)
+        return 0
 
     w = WORKLOADS[args.config]
     _log(f"generating {w.name} inputs")
@@ -321,6 +355,11 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
+    ceiling = None
+    if not args.no_ceiling:
+        _log("measuring the sustained MFMA rate")
+        ceiling = mfma_ceiling(bsa, torch)
+
     cpu = None
     if not args.no_cpu_baseline:
         _log("timing the CPU oracle on a bounded sample")
@@ -371,6 +410,8 @@ def main(argv=None):
         "speedup_attend_vs_dense": None if t_dense is None else round(t_dense / t_attend, 3),
         "score_hbm_gbs": round(score_bytes / (t_score * 1e-3) / 1e9, 1),
         "select_hbm_gbs": round(select_bytes / (t_select * 1e-3) / 1e9, 1),
+        "mfma_ceiling": ceiling,
+        "attend_frac_of_ceiling": None if ceiling is None else round(ach / ceiling["tflops"], 4),
         "roofline": {"kernel": "bsa_attend", "bound": "mfma", "achieved": round(ach, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic(w.name)},

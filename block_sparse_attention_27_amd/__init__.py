@@ -33,7 +33,7 @@ __all__ = [
     "Problem", "BsaError", "load_library", "library_path", "problem_for", "out_dtype",
     "bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_permute_rows", "bsa_attend",
     "bsa_attend_dense", "score", "score_ibcs", "score_stats", "select", "permute_rows", "with_kv_permuted",
-    "attend", "attend_dense", "sparse_attention", "SamplingPlan",
+    "attend", "attend_dense", "sparse_attention", "SamplingPlan", "bsa_mfma_ceiling", "MFMA_CEILING_FLOP",
     "BSA_OK", "BSA_ERR_INVALID_ARG", "BSA_ERR_UNSUPPORTED", "BSA_ERR_HIP", "BSA_BF16", "BSA_FP32",
 ]
 
@@ -109,6 +109,8 @@ def load_library():
     lib.bsa_attend.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_attend_dense.restype = ctypes.c_int
     lib.bsa_attend_dense.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.bsa_mfma_ceiling.restype = ctypes.c_int
+    lib.bsa_mfma_ceiling.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
     _lib = lib
     return lib
 
@@ -231,6 +233,17 @@ def bsa_permute_rows(p: Problem, x, perm, x_perm, stream=None):
     _expect("x_perm", x_perm, (p.B, p.H, p.N_pad, p.d), et)
     _check("bsa_permute_rows", load_library().bsa_permute_rows(ctypes.byref(p), _ptr(x), _ptr(perm), _ptr(x_perm),
                                                                _stream(stream)))
+
+
+# floating-point operations of one wave-round of bsa_mfma_ceiling: 8 MFMAs of 32 x 32 x 16 multiply-adds
+MFMA_CEILING_FLOP = 8 * 2 * 32 * 32 * 16
+
+
+def bsa_mfma_ceiling(out, iters: int, n_wg: int, stream=None):
+    """Measurement aid: n_wg workgroups of 4 waves, each wave `iters` rounds of 8 register-only MFMAs."""
+    import torch
+    _expect("out", out, (n_wg * 256,), torch.float32)
+    _check("bsa_mfma_ceiling", load_library().bsa_mfma_ceiling(_ptr(out), iters, n_wg, _stream(stream)))
 
 
 def bsa_attend(p: Problem, q, k, v, perm, idx, w, out, lse=None, stream=None):

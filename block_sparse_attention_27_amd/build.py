@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbsa.so")
 SOURCES = ["bsa_api.hip", "score.hip", "ibcs.hip", "select.hip", "permute.hip", "attend_bf16_d128.hip",
-           "attend_bf16_d64.hip", "attend_fp32.hip"]
+           "attend_bf16_d64.hip", "attend_fp32.hip", "measure.hip"]
 
 # Packed-fp32 instructions stay off (hipcc may otherwise form v_pk_* from float code).
 HIPFLAGS = [

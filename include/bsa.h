@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 5
+#define BSA_ABI_VERSION 6
 
 typedef enum bsa_status {
   BSA_OK = 0,
@@ -258,6 +258,30 @@ bsa_status bsa_attend(const bsa_problem* p, const void* q, const void* k, const 
  */
 bsa_status bsa_attend_dense(const bsa_problem* p, const void* q, const void* k, const void* v,
                             const int32_t* perm, void* out, float* lse, hipStream_t stream);
+
+/*
+ * bsa_mfma_ceiling -- a measurement aid, not a step of the method: the
+ * sustained rate of the bf16 matrix cores on this chip, against which the
+ * attention kernels' rates can be read. Under a long matrix load the chip
+ * lowers its clock to hold its power limit, so the published bf16 peak (at the
+ * top clock) is not reached even by a kernel that does nothing else.
+ *
+ * Launches n_wg workgroups of 4 waves (two per CU, as bsa_attend's kernel);
+ * every wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 on
+ * register operands, so the launch performs n_wg * 4 * iters * 8 * 32768
+ * floating-point operations and touches memory only to write `out`.
+ *   out  device, caller-owned, 4-byte aligned, n_wg * 256 floats: thread t of
+ *        workgroup g writes out[g * 256 + t] = 8 iters sum_r C[i_r][l % 32],
+ *        the sum of its accumulators, where lane l = t % 64 holds the A
+ *        fragment a_e = bf16(0.001 (l + e)) and the B fragment
+ *        b_e = bf16(0.002 (l - e)), e = 0..7, C = A B is their 32x32 product
+ *        (A[i][k] from lane i + 32 (k / 8), element k % 8; B[k][j] from lane
+ *        j + 32 (k / 8)), and i_r = 8 (r / 4) + 4 (l / 32) + r % 4.
+ * Time the launch with events on `stream` and divide the operations by it.
+ * Errors: out NULL or misaligned, iters < 1 or n_wg < 1 give
+ * BSA_ERR_INVALID_ARG (nothing launched); a failed launch BSA_ERR_HIP.
+ */
+bsa_status bsa_mfma_ceiling(float* out, int32_t iters, int32_t n_wg, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def _declared_functions():
 def test_header_declares_the_pipeline():
     names = _declared_functions()
     for n in ("bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_permute_rows", "bsa_attend",
-              "bsa_attend_dense", "bsa_status_string", "bsa_abi_version"):
+              "bsa_attend_dense", "bsa_status_string", "bsa_abi_version", "bsa_mfma_ceiling"):
         assert n in names
 
 
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 5
+    assert lib.bsa_abi_version() == 6
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(1) == b"invalid argument"
     assert lib.bsa_status_string(99) == b"unknown status"
@@ -191,6 +191,14 @@ def test_scoring_key_unit_limit_is_unsupported(lib):
     assert lib.bsa_score(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_UNSUPPORTED
     assert lib.bsa_score_ibcs(p, 4, 3, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_UNSUPPORTED
     assert lib.bsa_score_stats(p, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == bsa.BSA_ERR_UNSUPPORTED
+
+
+def test_mfma_ceiling_arguments_checked(lib):
+    assert lib.bsa_mfma_ceiling(None, 10, 4, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_mfma_ceiling(ctypes.c_void_p(0x7F0000000002), 10, 4, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_mfma_ceiling(FAKE, 0, 4, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_mfma_ceiling(FAKE, 10, 0, None) == bsa.BSA_ERR_INVALID_ARG
+    assert lib.bsa_mfma_ceiling(FAKE, -3, -1, None) == bsa.BSA_ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
