@@ -21,7 +21,9 @@ values. On the whole tensors, in the launch configuration of the full layers:
 * bsa_attend on 64-row query blocks and 64-key units, K and V gathered through
   the index inside (the 8-wave kernel);
 * fp32 Q, K and V (9.1 GB each): scores, selection and the fp32 attention
-  kernel, within 1e-5 of the oracle.
+  kernel, within 1e-5 of the oracle;
+* the clustering scorer through the gather index (group sizes bit-exact) and
+  the statistics-aware scorer.
 
 Bars as in the full-layer parity tests: scores 1e-3 relative, selection
 bit-exact, attention 2e-3 relative L2 and 1e-2 max-abs, lse 2e-3.
@@ -281,3 +283,37 @@ def test_fp32_inputs_past_2e31_elements(data):
                                                         W.select_seed, rows=rows)):
         assert np.array_equal(idx_all[b, h, i], ri), (b, h, i)
         assert np.array_equal(wt_all[b, h, i].view(np.uint32), rw.view(np.uint32)), (b, h, i)
+
+
+def test_alternative_scorers_past_2e31_elements(data):
+    """bsa_score_ibcs (G = 4, T = 3, through the gather index) and bsa_score_stats on the whole tensors."""
+    g, dev = data
+    q, k = dev["q"], dev["k"]
+    perm = g["perm"]
+    p = bsa.problem_for(W)
+    print_case(f"{W.name}: bsa_score_ibcs (G=4, T=3, permuted) and bsa_score_stats over {W.H} heads")
+    S_i, qc, qs, _ = bsa.score_ibcs(p, q, k, torch.from_numpy(perm).cuda(), groups=4, iters=3)
+    S_s, _, km, kv = bsa.score_stats(p, q, k)
+    torch.cuda.synchronize()
+    nQB = W.n_qblocks
+    n_rows = oracle.valid_counts(W.N, W.N_pad, W.block_q)
+    blocks = [0, nQB // 2, nQB - 1]
+    for h in (0, 33):
+        qh, kh = _host_head(g, "q", h), _host_head(g, "k", h)
+        rows, reps, sizes = oracle.score_ibcs(qh, kh, W.N, W.block_q, W.block_k, W.sm_scale, 4, 3, perm,
+                                              blocks=[(0, 0, i) for i in blocks])
+        for i, s_ref, c_ref, z_ref in zip(blocks, rows, reps, sizes):
+            z_got = qs[0, h, i].cpu().numpy()
+            assert np.array_equal(z_got, z_ref) and z_got.sum() == n_rows[i], (h, i, z_got, z_ref)
+            assert rel_l2(qc[0, h, i].cpu().numpy().astype(np.float64), c_ref) < 1e-5, (h, i)
+            got = S_i[0, h, i].cpu().numpy().astype(np.float64)
+            ref = s_ref.astype(np.float64)
+            assert not (np.abs(got - ref) > SCORE_RTOL * ref + 1e-12 * ref.max()).any(), (h, i)
+        S_ref, _, kb, kvar = oracle.score_stats(qh, kh, W.N, W.block_q, W.block_k, W.sm_scale)
+        assert rel_l2(km[0, h].cpu().numpy().astype(np.float64), kb[0, 0]) < 1e-5, h
+        assert rel_l2(kv[0, h].cpu().numpy().astype(np.float64), kvar[0, 0]) < 1e-5, h
+        got = S_s[0, h].cpu().numpy().astype(np.float64)
+        ref = S_ref[0, 0].astype(np.float64)
+        bad = np.abs(got - ref) > SCORE_RTOL * ref + 1e-12 * ref.max(axis=-1, keepdims=True)
+        assert not bad.any(), (h, int(bad.sum()))
+        print_case(f"  head {h}: clustering scorer (3 blocks) and statistics-aware scorer (whole head) match")
