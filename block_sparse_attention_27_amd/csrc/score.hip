@@ -181,8 +181,9 @@ constexpr int SC_CACHE_CHUNKS = 20;  // units up to 640: logits stay in LDS betw
 // and keeps, per lane, the running maximum and n_j-weighted sum of
 // 2^(x - max) with x = l log2(e); the lane halves and the waves combine them.
 // Pass 2 contracts the chunks again (the representatives and key means are
-// small and stay in L2) or, when every chunk's logits fit in LDS (up to 640
-// units), reads them back from there; it scales every lane's masses by its weight
+// small and stay in L2) or reads the logits back: from LDS when every chunk's
+// fit there (up to 640 units), else, with one representative per query block,
+// from S, where pass 1 left them; it scales every lane's masses by its weight
 // n_g / n, sums the G lanes of a query block, and writes S once: each wave
 // transposes its block through LDS so that every store instruction covers two
 // contiguous 128-byte row segments of S.
@@ -282,6 +283,16 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
   };
   auto keys_of = [&](int j) { return static_cast<float>(max(0, min(a.block_k, a.N - j * a.block_k))); };
 
+  // Rows too long for the LDS cache with one representative per query block
+  // (SPILL): pass 1 parks each lane's logits in its own query block's row of
+  // S, where pass 2 reads them back (the same lane, in program order) before
+  // the normalised values overwrite them, instead of contracting every chunk
+  // again.
+  constexpr bool SPILL = !CACHE && G == 1;
+  float* const lrow = a.S + (static_cast<size_t>(bh) * a.nQB + (qok ? qb : 0)) * a.nKU;
+  // 16-byte aligned rows of S (S itself need only be 4-byte aligned): four units per access
+  const bool vec4 = qok && a.nKU % 4 == 0 && reinterpret_cast<uintptr_t>(a.S) % 16 == 0;
+
   // ---- pass 1: running maximum and weighted sum per query block
   float run_m = -INFINITY, run_s = 0.f;
   for (int ch = wave; ch < n_chunks; ch += SC_WAVES) {
@@ -289,6 +300,18 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     if constexpr (CACHE) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) lcache[(ch * 16 + r) * 64 + lane] = acc[r];
+    } else if constexpr (SPILL) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {  // registers 4 g4 .. +3: units j .. j + 3
+        const int j = ch * 32 + 8 * g4 + 4 * h;
+        if (vec4 && j + 3 < a.nKU) {
+          *reinterpret_cast<f32x4*>(lrow + j) = f32x4{acc[4 * g4], acc[4 * g4 + 1], acc[4 * g4 + 2], acc[4 * g4 + 3]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (qok && j + e < a.nKU) lrow[j + e] = acc[4 * g4 + e];
+        }
+      }
     }
     float lmax = -INFINITY;
 #pragma unroll
@@ -339,6 +362,19 @@ __global__ __launch_bounds__(64 * SC_WAVES) void scores_kernel(ScoreArgs a) {
     if constexpr (CACHE) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = lcache[(ch * 16 + r) * 64 + lane];  // written by this lane
+    } else if constexpr (SPILL) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {  // written by this lane in pass 1; rows past nQB are never stored
+        const int j = ch * 32 + 8 * g4 + 4 * h;
+        if (vec4 && j + 3 < a.nKU) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(lrow + j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * g4 + e] = x[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * g4 + e] = (qok && j + e < a.nKU) ? lrow[j + e] : -INFINITY;
+        }
+      }
     } else {
       acc = logits(ch);
     }
