@@ -16,8 +16,10 @@ the intra-block clustering scorer in place of bsa_score, `stats` the
 statistics-aware scorer.
 `roofline` describes bsa_attend (bf16 MFMA bound), timed with HIP events on
 the stream it runs on; `mfma_ceiling` is the rate a register-only MFMA loop
-sustains on the same chip (its clock falls under a long matrix load), and
-`attend_frac_of_ceiling` bsa_attend's rate against it; `cpu_baseline` is the fp64 CPU oracle timed on a
+sustains on the same chip (below the top clock under a long matrix load), and
+`attend_frac_of_ceiling` bsa_attend's rate against it; with --power, `power`
+gives the socket power (amd-smi) while bsa_attend, then bsa_mfma_ceiling, run
+back to back, and the energy per floating-point operation of each; `cpu_baseline` is the fp64 CPU oracle timed on a
 bounded sample of the same workload on this host's cores.
 """
 
@@ -64,6 +66,69 @@ def _traffic(workload: str):
     if rec.get("attend_source_sha256_16") != attend_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _socket_power_w():
+    """Current socket power in watts from amd-smi (None when the tool or the field is missing)."""
+    import re
+    import shutil
+    import subprocess
+    tool = shutil.which("amd-smi") or ("/opt/rocm/bin/amd-smi" if os.path.exists("/opt/rocm/bin/amd-smi") else None)
+    if tool is None:
+        return None
+    try:
+        out = subprocess.run([tool, "metric", "-p", "-g", "0"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)
+    return float(m.group(1)) if m else None
+
+
+def power_under_load(torch, call, flop_per_call: float, seconds: float = 10.0) -> dict:
+    """Socket power while `call` runs back to back for about `seconds` (median of samples taken from
+    the middle of the run), the rate it sustains meanwhile, and the energy per floating-point operation."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        time.sleep(min(3.0, seconds / 3))  # let the clock and power settle first
+        while not stop.is_set():
+            v = _socket_power_w()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.5)
+
+    call()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0, n = time.perf_counter(), 0
+    th.start()
+    e0.record()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            call()
+        n += 10
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    ms = e0.elapsed_time(e1) / n
+    tf = flop_per_call / (ms * 1e-3) / 1e12
+    w = statistics.median(samples) if samples else None
+    return {"watts": w, "samples": len(samples), "ms_per_call": round(ms, 3), "tflops": round(tf, 1),
+            "pj_per_flop": None if w is None else round(w / (tf * 1e12) * 1e12, 3)}
+
+
+def power_report(bsa, torch, attend_call, exec_flops: float) -> dict:
+    """Idle socket power, then bsa_attend and bsa_mfma_ceiling each run back to back with power sampled."""
+    idle = _socket_power_w()
+    att = power_under_load(torch, attend_call, exec_flops)
+    cout = torch.empty(512 * 256, dtype=torch.float32, device="cuda")
+    ceil = power_under_load(torch, lambda: bsa.bsa_mfma_ceiling(cout, 40000, 512),
+                            512 * 4 * 40000 * bsa.MFMA_CEILING_FLOP)
+    return {"idle_watts": idle, "bsa_attend": att, "mfma_ceiling": ceil}
 
 
 def cpu_baseline(w, g, budget_s: float = 20.0):
@@ -118,8 +183,9 @@ def cpu_baseline(w, g, budget_s: float = 20.0):
 def mfma_ceiling(bsa, torch, iters: int = 40000, n_wg: int = 512, reps: int = 5) -> dict:
     """Sustained bf16 MFMA rate of this chip: bsa_mfma_ceiling, 2 workgroups per CU, ~10 ms per launch.
 
-    Under a long matrix load the clock drops to hold the power limit, so this
-    register-only loop is the ceiling any matrix-bound kernel meets here.
+    Under a long matrix load the clock stays well below the top clock (the chip
+    runs at or near its power limit), so this register-only loop is the
+    ceiling any matrix-bound kernel meets here.
     """
     stream = torch.cuda.current_stream()
     out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
@@ -153,6 +219,10 @@ def main(argv=None):
     ap.add_argument("--no-ceiling", action="store_true", help="skip the sustained-MFMA-rate measurement")
     ap.add_argument("--ceiling-only", action="store_true",
                     help="only measure the sustained MFMA rate (bsa_mfma_ceiling) and print it")
+    ap.add_argument("--power", action="store_true",
+                    help="also sample socket power (amd-smi) under bsa_attend and under bsa_mfma_ceiling")
+    ap.add_argument("--power-only", action="store_true",
+                    help="only the power samples: bsa_attend on the config's lists, then bsa_mfma_ceiling")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -221,6 +291,15 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    def attend_call():
+        bsa.bsa_attend(pp, q, kk, vv, perm, idx, wt, out, None)
+
+    if args.power_only:
+        _log("sampling socket power under bsa_attend, then under bsa_mfma_ceiling")
+        print(json.dumps({"config": w.name, "power": power_report(bsa, torch, attend_call, w.executed_flops())}),
+              flush=True)
+        return 0
 
     _log(f"timing {args.steps} steps")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -355,6 +434,11 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
 
+    power = None
+    if args.power:
+        _log("sampling socket power under bsa_attend, then under bsa_mfma_ceiling")
+        power = power_report(bsa, torch, attend_call, exec_flops)
+
     ceiling = None
     if not args.no_ceiling:
         _log("measuring the sustained MFMA rate")
@@ -411,6 +495,7 @@ def main(argv=None):
         "score_hbm_gbs": round(score_bytes / (t_score * 1e-3) / 1e9, 1),
         "select_hbm_gbs": round(select_bytes / (t_select * 1e-3) / 1e9, 1),
         "mfma_ceiling": ceiling,
+        "power": power,
         "attend_frac_of_ceiling": None if ceiling is None else round(ach / ceiling["tflops"], 4),
         "roofline": {"kernel": "bsa_attend", "bound": "mfma", "achieved": round(ach, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),

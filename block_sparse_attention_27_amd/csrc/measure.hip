@@ -1,12 +1,13 @@
 // Measurement aid: the sustained rate of the bf16 matrix cores.
 //
 // The published bf16 peak assumes the top clock. Under a long matrix load the
-// chip holds its power limit by lowering the clock, so the rate a kernel can
-// reach is set by what else it spends power on. This kernel spends it on
-// nothing else: every wave keeps 8 independent v_mfma_f32_32x32x16_bf16 chains
-// on register operands (no memory traffic, no other vector work in the loop),
-// in workgroups of 4 waves, two per CU as in the attention kernel. Its rate is
-// the ceiling a matrix-bound kernel meets on the same chip and clock policy.
+// chip runs well below it (at or near its socket power limit), so the rate a
+// kernel can reach is set by what else it spends energy on. This kernel spends
+// it on nothing else: every wave keeps 8 independent v_mfma_f32_32x32x16_bf16
+// chains on register operands (no memory traffic, no other vector work in the
+// loop), in workgroups of 4 waves, two per CU as in the attention kernel. Its
+// rate is the ceiling a matrix-bound kernel meets on the same chip and clock
+// policy.
 #include "bsa_internal.hpp"
 
 namespace bsa {

@@ -263,8 +263,9 @@ bsa_status bsa_attend_dense(const bsa_problem* p, const void* q, const void* k, 
  * bsa_mfma_ceiling -- a measurement aid, not a step of the method: the
  * sustained rate of the bf16 matrix cores on this chip, against which the
  * attention kernels' rates can be read. Under a long matrix load the chip
- * lowers its clock to hold its power limit, so the published bf16 peak (at the
- * top clock) is not reached even by a kernel that does nothing else.
+ * runs well below its top clock, at or near its socket power limit, so the
+ * published bf16 peak (at the top clock) is not reached even by a kernel that
+ * does nothing else.
  *
  * Launches n_wg workgroups of 4 waves (two per CU, as bsa_attend's kernel);
  * every wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 on
