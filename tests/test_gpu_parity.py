@@ -204,6 +204,29 @@ def test_layer_score_select_attend(name):
     del out, lse, out16
 
 
+@pytest.mark.parametrize("name,heads", [("wan14b_720p", None), ("hunyuan", None)])
+def test_layer_attention_every_query_block(name, heads):
+    """bsa_attend against the oracle on every query block of whole heads (every head at 720p), fed the GPU's lists;
+    the oracle runs one head per CPU worker."""
+    import oracle_pool
+    w, g, dev = workload_data(name)
+    p = bsa.problem_for(w, out_fp32=1)
+    print_case(f"{name}: the pass on the GPU, then the oracle on every query block of "
+               f"{'all' if heads is None else len(heads)} heads")
+    S, _, _ = bsa.score(p, dev["q"], dev["k"], dev["perm"])
+    idx, wt = bsa.select(p, S)
+    out, lse = bsa.attend(p, dev["q"], dev["k"], dev["v"], idx, wt, dev["perm"], with_lse=True)
+    torch.cuda.synchronize()
+    recs = oracle_pool.attend_heads(g["q"], g["k"], g["v"], idx.cpu().numpy(), wt.cpu().numpy(), out.cpu().numpy(),
+                                    lse.cpu().numpy(), w.N, w.block_q, w.block_k, w.sm_scale, g["perm"], heads=heads)
+    rel = float(np.sqrt(sum(r["ss_diff"] for r in recs) / sum(r["ss_ref"] for r in recs)))
+    mx = max(r["max_abs"] for r in recs)
+    ml = max(r["max_lse"] for r in recs)
+    print_case(f"  {len(recs)} heads x {w.n_qblocks} blocks: rel_l2={rel:.3e} max_abs={mx:.3e} max_lse={ml:.3e}")
+    assert all(r["pad_zero"] and r["lse_finite_match"] for r in recs)
+    assert rel <= OUT_REL_L2 and mx <= OUT_MAX_ABS and ml < LSE_ABS, (rel, mx, ml)
+
+
 @pytest.mark.parametrize("name", ["wan13b", "wan14b_720p", "hunyuan"])
 def test_layer_dense(name):
     print_case(f"{name}: bsa_attend_dense vs oracle")
