@@ -169,10 +169,10 @@ def test_tiny_fp32_end_to_end():
 # ------------------------------------------------------------- full-size layers
 
 LAYERS = {
-    # name: (heads checked for S, (heads, blocks) for attention, rows for selection)
-    "wan13b": (2, (2, 8), 400),
-    "wan14b_720p": (2, (2, 6), 300),
-    "hunyuan": (1, (2, 4), 80),
+    # name: (heads checked for S, (heads, blocks) for attention, rows for selection); None: every head
+    "wan13b": (None, (2, 8), 400),
+    "wan14b_720p": (None, (2, 6), 300),
+    "hunyuan": (None, (2, 4), 80),
 }
 
 
@@ -188,8 +188,8 @@ def test_layer_score_select_attend(name):
     torch.cuda.synchronize()
     out, lse, out16 = run_attend(p, dev, idx, wt)
 
-    print_case(f"{name}: scores vs oracle")
-    check_scores(w, g, S, list(range(n_s_heads)))
+    print_case(f"{name}: scores vs oracle on every head")
+    check_scores(w, g, S, list(range(w.H if n_s_heads is None else n_s_heads)))
 
     print_case(f"{name}: selection bit-exactness on {n_rows} sampled rows")
     rng = np.random.default_rng(1)
