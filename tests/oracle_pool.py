@@ -27,7 +27,9 @@ def select_rows(S: np.ndarray, N: int, block_k: int, k: int, m: int, seed: int, 
     n_valid = -(-N // block_k)
     workers = max(1, min(workers, len(os.sched_getaffinity(0))))
     n_chunks = max(1, min(len(rows), 4 * workers))
-    chunks = [rows[c::n_chunks] for c in range(n_chunks)]
+    # contiguous runs of the row list: rows listed head by head give each chunk one or two (b, h) slices
+    bounds = [len(rows) * c // n_chunks for c in range(n_chunks + 1)]
+    chunks = [rows[bounds[c]:bounds[c + 1]] for c in range(n_chunks)]
     # only the (b, h) slices a chunk reads travel to its worker
     jobs = [({(b, h): S[b, h] for b, h in {(b, h) for b, h, _ in ch}}, n_valid, k, m, seed, ch) for ch in chunks]
     ctx = multiprocessing.get_context("spawn")
@@ -36,8 +38,8 @@ def select_rows(S: np.ndarray, N: int, block_k: int, k: int, m: int, seed: int, 
     idx = np.empty((len(rows), k + m), dtype=np.int32)
     w = np.empty((len(rows), k + m), dtype=np.float32)
     for c, (ri, rw) in enumerate(outs):
-        idx[c::n_chunks] = ri
-        w[c::n_chunks] = rw
+        idx[bounds[c]:bounds[c + 1]] = ri
+        w[bounds[c]:bounds[c + 1]] = rw
     return idx, w
 
 

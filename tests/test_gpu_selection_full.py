@@ -4,10 +4,9 @@ Bar: idx and the bit patterns of w equal the oracle's, fed the same fp32 S
 (InstaGen, Abstract: one random draw per query block, shared by its queries;
 the draw is word 0 of Philox4x32-10 at counter (i, h, b, 0) and key = seed).
 
-* every one of the 23,640 rows of the Wan2.1-14B 720p layer (40 heads x 591
-  query blocks, 591 units per row), S from bsa_score on the GPU;
-* 10,220 rows of the HunyuanVideo layer (every query block of 11 heads, 3,713
-  valid 32-key units per row, the long-row kernel), S from bsa_score;
+* every row of the Wan2.1-1.3B (3,072 rows of 256 units), 480p (10,240 rows),
+  720p (23,640 rows of 591 units) and HunyuanVideo (22,296 rows of 3,713 valid
+  32-key units, the long-row kernel) layers, S from bsa_score on the GPU;
 * a sweep of 20 seeds over a 2-head 480p-shaped layer: 10,240 (counter, key)
   pairs;
 * 10,000 seeds on four 16-unit rows, every (seed, row) bit-exact, and the
@@ -57,23 +56,14 @@ def _compare(w, p, S, idx, wt, rows, seed):
     print_case(f"  {len(rows)} rows bit-exact")
 
 
-def test_selection_every_row_of_the_720p_layer():
-    w = WORKLOADS["wan14b_720p"]
+@pytest.mark.parametrize("name", ["wan13b", "wan14b_480p", "wan14b_720p", "hunyuan"])
+def test_selection_every_row_of_the_layer(name):
+    w = WORKLOADS[name]
     p = bsa.problem_for(w)
-    print_case(f"720p: score + select on the GPU, all {w.B * w.H * w.n_qblocks} rows vs the oracle")
+    print_case(f"{name}: score + select on the GPU, all {w.B * w.H * w.n_qblocks} rows "
+               f"({w.n_valid_units} valid units each) vs the oracle")
     S, idx, wt = _gpu_scores_and_lists(w, p)
     rows = [(b, h, i) for b in range(w.B) for h in range(w.H) for i in range(w.n_qblocks)]
-    _compare(w, p, S, idx, wt, rows, w.select_seed)
-
-
-def test_selection_hunyuan_ten_thousand_rows():
-    w = WORKLOADS["hunyuan"]
-    p = bsa.problem_for(w)
-    print_case("hunyuan: score + select on the GPU, every query block of heads 0..10 vs the oracle")
-    S, idx, wt = _gpu_scores_and_lists(w, p)
-    rows = [(0, h, i) for h in range(11) for i in range(w.n_qblocks)]
-    rows.append((0, w.H - 1, w.n_qblocks - 1))
-    assert len(rows) >= 10_000
     _compare(w, p, S, idx, wt, rows, w.select_seed)
 
 
