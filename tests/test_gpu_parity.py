@@ -204,7 +204,7 @@ def test_layer_score_select_attend(name):
     del out, lse, out16
 
 
-@pytest.mark.parametrize("name,heads", [("wan14b_720p", None), ("hunyuan", None)])
+@pytest.mark.parametrize("name,heads", [("wan13b", None), ("wan14b_480p", None), ("wan14b_720p", None), ("hunyuan", None)])
 def test_layer_attention_every_query_block(name, heads):
     """bsa_attend against the oracle on every query block of whole heads (every head at 720p), fed the GPU's lists;
     the oracle runs one head per CPU worker."""
