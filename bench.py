@@ -17,8 +17,11 @@ statistics-aware scorer.
 `roofline` describes bsa_attend (bf16 MFMA bound), timed with HIP events on
 the stream it runs on; `mfma_ceiling` is the rate a register-only MFMA loop
 sustains on the same chip (below the top clock under a long matrix load), and
-`attend_frac_of_ceiling` bsa_attend's rate against it; with --power, `power`
-gives the socket power (amd-smi) while bsa_attend, then bsa_mfma_ceiling, run
+`attend_frac_of_ceiling` bsa_attend's rate against it; `mfma_ceiling_random`
+and `attend_frac_of_random_ceiling` the same for the loop on operands that
+change from one product to the next (bsa_mfma_ceiling_random: data that toggles
+bits costs energy, and energy sets the clock at the power limit); with --power,
+`power` gives the socket power (amd-smi) while bsa_attend, then both loops, run
 back to back, and the energy per floating-point operation of each; `cpu_baseline` is the fp64 CPU oracle timed on a
 bounded sample of the same workload on this host's cores.
 """
@@ -122,13 +125,25 @@ def power_under_load(torch, call, flop_per_call: float, seconds: float = 10.0) -
 
 
 def power_report(bsa, torch, attend_call, exec_flops: float) -> dict:
-    """Idle socket power, then bsa_attend and bsa_mfma_ceiling each run back to back with power sampled."""
-    idle = _socket_power_w()
+    """Idle socket power, then bsa_attend and both MFMA loops each run back to back with power sampled.
+
+    The idle figure is the lowest of samples taken over 4 s with the GPU idle: the reading averages over a
+    window, so one taken right after a load still carries it."""
+    torch.cuda.synchronize()
+    idle_samples = []
+    for _ in range(8):
+        time.sleep(0.5)
+        v = _socket_power_w()
+        if v is not None:
+            idle_samples.append(v)
+    idle = min(idle_samples) if idle_samples else None
     att = power_under_load(torch, attend_call, exec_flops)
     cout = torch.empty(512 * 256, dtype=torch.float32, device="cuda")
     ceil = power_under_load(torch, lambda: bsa.bsa_mfma_ceiling(cout, 40000, 512),
                             512 * 4 * 40000 * bsa.MFMA_CEILING_FLOP)
-    return {"idle_watts": idle, "bsa_attend": att, "mfma_ceiling": ceil}
+    ceil_r = power_under_load(torch, lambda: bsa.bsa_mfma_ceiling_random(cout, 40000, 512),
+                              512 * 4 * 40000 * bsa.MFMA_CEILING_FLOP)
+    return {"idle_watts": idle, "bsa_attend": att, "mfma_ceiling": ceil, "mfma_ceiling_random": ceil_r}
 
 
 def cpu_baseline(w, g, budget_s: float = 20.0):
@@ -180,30 +195,35 @@ def cpu_baseline(w, g, budget_s: float = 20.0):
                         "attend_per_block": round(t_attend_block, 5)}}
 
 
-def mfma_ceiling(bsa, torch, iters: int = 40000, n_wg: int = 512, reps: int = 5) -> dict:
+def mfma_ceiling(bsa, torch, iters: int = 40000, n_wg: int = 512, reps: int = 5, random: bool = False) -> dict:
     """Sustained bf16 MFMA rate of this chip: bsa_mfma_ceiling, 2 workgroups per CU, ~10 ms per launch.
 
     Under a long matrix load the clock stays well below the top clock (the chip
     runs at or near its power limit), so this register-only loop is the
-    ceiling any matrix-bound kernel meets here.
+    ceiling any matrix-bound kernel meets here. random=True times
+    bsa_mfma_ceiling_random, whose operands change from one product to the
+    next as real data does (iters must then be a multiple of 4).
     """
     stream = torch.cuda.current_stream()
     out = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    probe = bsa.bsa_mfma_ceiling_random if random else bsa.bsa_mfma_ceiling
     for _ in range(2):
-        bsa.bsa_mfma_ceiling(out, iters, n_wg)
+        probe(out, iters, n_wg)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
     for e in ev:
         e[0].record(stream)
-        bsa.bsa_mfma_ceiling(out, iters, n_wg)
+        probe(out, iters, n_wg)
         e[1].record(stream)
     torch.cuda.synchronize()
     ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
     flop = n_wg * 4 * iters * bsa.MFMA_CEILING_FLOP
     tf = flop / (ms * 1e-3) / 1e12
     return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "ms_per_launch": round(ms, 3),
-            "kernel": f"bsa_mfma_ceiling: {n_wg} workgroups of 4 waves, {iters} rounds of 8 register-only "
-                      "v_mfma_f32_32x32x16_bf16 per wave"}
+            "kernel": f"{'bsa_mfma_ceiling_random' if random else 'bsa_mfma_ceiling'}: {n_wg} workgroups of 4 waves, "
+                      f"{iters} rounds of 8 register-only v_mfma_f32_32x32x16_bf16 per wave"
+                      + (" on operands that change from one product to the next" if random else
+                         " on constant operands")}
 
 
 def main(argv=None):
@@ -238,7 +258,8 @@ def main(argv=None):
     from block_sparse_attention_27_amd.inputs import WORKLOADS, generate
 
     if args.ceiling_only:
-        print(json.dumps({"mfma_ceiling": mfma_ceiling(bsa, torch)}), flush=True)
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(bsa, torch),
+                          "mfma_ceiling_random": mfma_ceiling(bsa, torch, random=True)}), flush=True)
         return 0
 
     w = WORKLOADS[args.config]
@@ -296,7 +317,7 @@ def main(argv=None):
         bsa.bsa_attend(pp, q, kk, vv, perm, idx, wt, out, None)
 
     if args.power_only:
-        _log("sampling socket power under bsa_attend, then under bsa_mfma_ceiling")
+        _log("sampling socket power under bsa_attend, then under both MFMA loops")
         print(json.dumps({"config": w.name, "power": power_report(bsa, torch, attend_call, w.executed_flops())}),
               flush=True)
         return 0
@@ -436,13 +457,14 @@ def main(argv=None):
 
     power = None
     if args.power:
-        _log("sampling socket power under bsa_attend, then under bsa_mfma_ceiling")
+        _log("sampling socket power under bsa_attend, then under both MFMA loops")
         power = power_report(bsa, torch, attend_call, exec_flops)
 
-    ceiling = None
+    ceiling = ceiling_r = None
     if not args.no_ceiling:
         _log("measuring the sustained MFMA rate")
         ceiling = mfma_ceiling(bsa, torch)
+        ceiling_r = mfma_ceiling(bsa, torch, random=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -497,6 +519,8 @@ def main(argv=None):
         "mfma_ceiling": ceiling,
         "power": power,
         "attend_frac_of_ceiling": None if ceiling is None else round(ach / ceiling["tflops"], 4),
+        "mfma_ceiling_random": ceiling_r,
+        "attend_frac_of_random_ceiling": None if ceiling_r is None else round(ach / ceiling_r["tflops"], 4),
         "roofline": {"kernel": "bsa_attend", "bound": "mfma", "achieved": round(ach, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic(w.name)},

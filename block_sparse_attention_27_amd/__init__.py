@@ -33,7 +33,7 @@ __all__ = [
     "Problem", "BsaError", "load_library", "library_path", "problem_for", "out_dtype",
     "bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_permute_rows", "bsa_attend",
     "bsa_attend_dense", "score", "score_ibcs", "score_stats", "select", "permute_rows", "with_kv_permuted",
-    "attend", "attend_dense", "sparse_attention", "SamplingPlan", "bsa_mfma_ceiling", "MFMA_CEILING_FLOP",
+    "attend", "attend_dense", "sparse_attention", "SamplingPlan", "bsa_mfma_ceiling", "bsa_mfma_ceiling_random", "MFMA_CEILING_FLOP",
     "BSA_OK", "BSA_ERR_INVALID_ARG", "BSA_ERR_UNSUPPORTED", "BSA_ERR_HIP", "BSA_BF16", "BSA_FP32",
 ]
 
@@ -111,6 +111,8 @@ def load_library():
     lib.bsa_attend_dense.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.bsa_mfma_ceiling.restype = ctypes.c_int
     lib.bsa_mfma_ceiling.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
+    lib.bsa_mfma_ceiling_random.restype = ctypes.c_int
+    lib.bsa_mfma_ceiling_random.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp]
     _lib = lib
     return lib
 
@@ -244,6 +246,14 @@ def bsa_mfma_ceiling(out, iters: int, n_wg: int, stream=None):
     import torch
     _expect("out", out, (n_wg * 256,), torch.float32)
     _check("bsa_mfma_ceiling", load_library().bsa_mfma_ceiling(_ptr(out), iters, n_wg, _stream(stream)))
+
+
+def bsa_mfma_ceiling_random(out, iters: int, n_wg: int, stream=None):
+    """Measurement aid: as bsa_mfma_ceiling, with operands that change from one MFMA to the next."""
+    import torch
+    _expect("out", out, (n_wg * 256,), torch.float32)
+    _check("bsa_mfma_ceiling_random",
+           load_library().bsa_mfma_ceiling_random(_ptr(out), iters, n_wg, _stream(stream)))
 
 
 def bsa_attend(p: Problem, q, k, v, perm, idx, w, out, lse=None, stream=None):

@@ -212,7 +212,13 @@ bsa_status bsa_attend_dense(const bsa_problem* p, const void* q, const void* k, 
 
 bsa_status bsa_mfma_ceiling(float* out, int32_t iters, int32_t n_wg, hipStream_t stream) {
   if (!out || !aligned(out, 4) || iters < 1 || n_wg < 1) return BSA_ERR_INVALID_ARG;
-  return from_hip(bsa::launch_mfma_ceiling(out, iters, n_wg, stream));
+  return from_hip(bsa::launch_mfma_ceiling(out, iters, n_wg, false, stream));
+}
+
+bsa_status bsa_mfma_ceiling_random(float* out, int32_t iters, int32_t n_wg, hipStream_t stream) {
+  if (!out || !aligned(out, 4) || iters < 4 || iters % 4 != 0 || n_wg < 1 || n_wg > (1 << 18))
+    return BSA_ERR_INVALID_ARG;
+  return from_hip(bsa::launch_mfma_ceiling(out, iters, n_wg, true, stream));
 }
 
 }  // extern "C"

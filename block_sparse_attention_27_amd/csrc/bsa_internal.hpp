@@ -35,7 +35,7 @@ hipError_t launch_block_clusters(const Geometry& g, int groups, int iters, const
 // x_perm[b][h][r] = x[b][h][perm[r]] for r < N (a zero row for an entry
 // outside [0, N_pad)); rows N .. N_pad-1 of x_perm are zero
 hipError_t launch_permute_rows(const Geometry& g, const void* x, const int32_t* perm, void* x_perm, hipStream_t s);
-hipError_t launch_mfma_ceiling(float* out, int iters, int n_wg, hipStream_t s);
+hipError_t launch_mfma_ceiling(float* out, int iters, int n_wg, bool random_operands, hipStream_t s);
 
 // ---- selection ----
 hipError_t launch_select(const Geometry& g, int k_exact, int m_sample, const float* S, int32_t* idx,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 6
+#define BSA_ABI_VERSION 7
 
 typedef enum bsa_status {
   BSA_OK = 0,
@@ -283,6 +283,27 @@ bsa_status bsa_attend_dense(const bsa_problem* p, const void* q, const void* k, 
  * BSA_ERR_INVALID_ARG (nothing launched); a failed launch BSA_ERR_HIP.
  */
 bsa_status bsa_mfma_ceiling(float* out, int32_t iters, int32_t n_wg, hipStream_t stream);
+
+/*
+ * bsa_mfma_ceiling_random -- the same measurement aid on data that changes
+ * from one product to the next. A product's energy depends on how many
+ * operand bits toggle, and at the power limit energy sets the clock, so
+ * constant operands overstate what products over real data can sustain.
+ *
+ * Same launch and operation count as bsa_mfma_ceiling. Thread t of workgroup
+ * g (n = 256 g + t, lane l = t % 64) holds four A fragments
+ * a_f[e] = bf16(v(64 n + 8 f + e)) and four B fragments
+ * b_f[e] = bf16(v(64 n + 32 + 8 f + e + l)), f = 0..3, e = 0..7, where v(x)
+ * in [-2, 2) is the top 24 bits of Wellons' lowbias32 hash of x as a
+ * fraction, times 4, minus 2. Round 4 j + u multiplies into chain c
+ * (c = 0..7) the fragments a_((c + u) mod 4) and b_((c / 2 + 3 u) mod 4).
+ *   out  as for bsa_mfma_ceiling: the sum of the thread's 8 x 16 accumulators
+ *        (C[i_r][l % 32] summed over its rows i_r, over every round and chain).
+ * Errors: out NULL or misaligned, iters < 4 or not a multiple of 4, n_wg < 1
+ * or above 2^18 give BSA_ERR_INVALID_ARG (nothing launched); a failed launch
+ * BSA_ERR_HIP.
+ */
+bsa_status bsa_mfma_ceiling_random(float* out, int32_t iters, int32_t n_wg, hipStream_t stream);
 
 #ifdef __cplusplus
 }

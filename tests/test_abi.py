@@ -33,7 +33,7 @@ def _declared_functions():
 def test_header_declares_the_pipeline():
     names = _declared_functions()
     for n in ("bsa_score", "bsa_score_ibcs", "bsa_score_stats", "bsa_select", "bsa_permute_rows", "bsa_attend",
-              "bsa_attend_dense", "bsa_status_string", "bsa_abi_version", "bsa_mfma_ceiling"):
+              "bsa_attend_dense", "bsa_status_string", "bsa_abi_version", "bsa_mfma_ceiling", "bsa_mfma_ceiling_random"):
         assert n in names
 
 
@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.bsa_abi_version() == 6
+    assert lib.bsa_abi_version() == 7
     assert lib.bsa_status_string(0) == b"ok"
     assert lib.bsa_status_string(1) == b"invalid argument"
     assert lib.bsa_status_string(99) == b"unknown status"
@@ -199,6 +199,13 @@ def test_mfma_ceiling_arguments_checked(lib):
     assert lib.bsa_mfma_ceiling(FAKE, 0, 4, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_mfma_ceiling(FAKE, 10, 0, None) == bsa.BSA_ERR_INVALID_ARG
     assert lib.bsa_mfma_ceiling(FAKE, -3, -1, None) == bsa.BSA_ERR_INVALID_ARG
+    f = lib.bsa_mfma_ceiling_random
+    assert f(None, 8, 4, None) == bsa.BSA_ERR_INVALID_ARG
+    assert f(ctypes.c_void_p(0x7F0000000002), 8, 4, None) == bsa.BSA_ERR_INVALID_ARG
+    for iters in (0, 1, 2, 3, 6, -4):  # rounds come in fours
+        assert f(FAKE, iters, 4, None) == bsa.BSA_ERR_INVALID_ARG
+    assert f(FAKE, 8, 0, None) == bsa.BSA_ERR_INVALID_ARG
+    assert f(FAKE, 8, (1 << 18) + 1, None) == bsa.BSA_ERR_INVALID_ARG
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

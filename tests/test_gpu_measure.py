@@ -51,6 +51,63 @@ def test_output_is_the_fragment_product():
     assert np.allclose(got, ref[None, :], rtol=1e-5, atol=1e-6 * np.abs(ref).max()), np.abs(got - ref).max()
 
 
+def _lowbias32(x: np.ndarray) -> np.ndarray:
+    """Wellons' lowbias32 integer hash on uint32 arrays (arithmetic mod 2^32)."""
+    x = x.astype(np.uint64)
+    m = np.uint64(0xFFFFFFFF)
+    x ^= x >> np.uint64(16)
+    x = (x * np.uint64(0x7FEB352D)) & m
+    x ^= x >> np.uint64(15)
+    x = (x * np.uint64(0x846CA68B)) & m
+    x ^= x >> np.uint64(16)
+    return x
+
+
+def _expected_random(iters: int, n_wg: int) -> np.ndarray:
+    """Per thread: the sum of its accumulators for the hashed fragments of bsa_mfma_ceiling_random."""
+    n = np.arange(n_wg * 256, dtype=np.uint64)
+    lane = (n % np.uint64(64))
+    f = np.arange(4, dtype=np.uint64)[None, :, None]
+    e = np.arange(8, dtype=np.uint64)[None, None, :]
+    base = (n * np.uint64(64))[:, None, None]
+
+    def val(x):
+        v = (_lowbias32(x) >> np.uint64(8)).astype(np.float64) * (4.0 / 16777216.0) - 2.0
+        return torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).double().numpy()
+
+    a = val(base + np.uint64(8) * f + e)                                        # [thread, f, e]
+    b = val(base + np.uint64(32) + np.uint64(8) * f + e + lane[:, None, None])  # [thread, f, e]
+    out = np.empty(n_wg * 256)
+    for wv in range(n_wg * 4):
+        t = np.arange(64) + 64 * wv
+        A = np.empty((4, 32, 16))
+        B = np.empty((4, 16, 32))
+        for k in range(16):
+            A[:, :, k] = a[t[np.arange(32) + 32 * (k // 8)], :, k % 8].T
+            B[:, k, :] = b[t[np.arange(32) + 32 * (k // 8)], :, k % 8].T
+        T = np.zeros((32, 32))
+        for c in range(8):
+            for u in range(4):
+                T += A[(c + u) % 4] @ B[(c // 2 + 3 * u) % 4]
+        T *= iters // 4
+        for l in range(64):
+            rows = [8 * (r // 4) + 4 * (l // 32) + r % 4 for r in range(16)]
+            out[t[l]] = T[rows, l % 32].sum()
+    return out
+
+
+def test_random_operand_output_is_the_fragment_product():
+    print_case("bsa_mfma_ceiling_random: 8 rounds, 2 workgroups, against the products of its hashed fragments")
+    iters, n_wg = 8, 2
+    out = torch.full((n_wg * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    bsa.bsa_mfma_ceiling_random(out, iters, n_wg)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = _expected_random(iters, n_wg)
+    # fp32 accumulation of 16 x 16 x 8 x 8 products of magnitude <= 4: a few ulps of the partial sums
+    assert np.allclose(got, ref, rtol=1e-4, atol=1e-4 * np.abs(ref).max()), np.abs(got - ref).max()
+
+
 def test_rate_is_between_attention_and_peak():
     import bench
     print_case("bsa_mfma_ceiling: sustained rate, 512 workgroups, ~10 ms launches")
@@ -58,3 +115,6 @@ def test_rate_is_between_attention_and_peak():
     print_case(f"  {r['tflops']} TFLOP/s ({r['frac_of_peak'] * 100:.1f}% of {bench.PEAK_BF16_TFLOPS:.0f})")
     # at least what the attention kernel sustains, at most the published peak
     assert 1000.0 < r["tflops"] <= bench.PEAK_BF16_TFLOPS
+    rr = bench.mfma_ceiling(bsa, torch, iters=40000, n_wg=512, reps=3, random=True)
+    print_case(f"  random operands: {rr['tflops']} TFLOP/s ({rr['frac_of_peak'] * 100:.1f}%)")
+    assert 1000.0 < rr["tflops"] <= bench.PEAK_BF16_TFLOPS
