@@ -232,6 +232,11 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="wan14b_720p")
+    ap.add_argument("--seed", type=int, default=None, help="generator seed of the synthetic inputs (preset: 0)")
+    ap.add_argument("--select-seed", type=int, default=None, help="Philox key of the selection (preset: 0)")
+    ap.add_argument("--temperature", type=float, default=None,
+                    help="logit temperature, sm_scale = 1 / temperature (preset: the config's)")
+    ap.add_argument("--heads", type=int, default=None, help="number of heads H (preset: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -263,6 +268,11 @@ def main(argv=None):
         return 0
 
     w = WORKLOADS[args.config]
+    overrides = {name: val for name, val in (("seed", args.seed), ("select_seed", args.select_seed),
+                                             ("temperature", args.temperature), ("H", args.heads))
+                 if val is not None}
+    if overrides:
+        w = w.replace(**overrides)
     _log(f"generating {w.name} inputs")
     g = generate(w)
 
@@ -487,7 +497,10 @@ def main(argv=None):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_pad": w.N_pad, "d": w.d,
                    "block_q": w.block_q, "block_k": w.block_k, "k_exact": w.k_exact,
                    "m_sample": w.m_sample, "density": round(w.density, 4), "temperature": w.temperature,
-                   "permuted": w.permute, "parallelism": "single GPU"},
+                   "permuted": w.permute, "seed": w.seed, "select_seed": w.select_seed,
+                   "parallelism": "single GPU"},
+        "device": {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+                   "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None)},
         "t_permute_ms": round(t_permute, 4) if perm is not None else None,
         "t_score_ms": round(t_score, 4),
         "t_select_ms": round(t_select, 4),
@@ -523,7 +536,7 @@ def main(argv=None):
         "attend_frac_of_random_ceiling": None if ceiling_r is None else round(ach / ceiling_r["tflops"], 4),
         "roofline": {"kernel": "bsa_attend", "bound": "mfma", "achieved": round(ach, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                     "traffic": _traffic(w.name)},
+                     "traffic": None if overrides else _traffic(w.name)},  # counters were taken on the preset
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
